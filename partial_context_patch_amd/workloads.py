@@ -1,0 +1,131 @@
+"""Seeded synthetic workloads shaped like the pages' diffusion attention layers.
+
+This module is the only code that both the HIP path's tests/benchmark and the
+CPU oracle consume.  It draws random tensors and rounds them to the storage
+dtype; it holds none of the attention method's arithmetic (no halo sizes, no
+membership, no softmax).
+
+Value recipe (all seeded with numpy's PCG64):
+* Q, K, V ~ N(0, 1), drawn in fp32 in that order;
+* stale K/V (strip workloads only) = fresh + N(0, 0.05^2) noise, drawn next;
+* FLUX-shaped workload: Q and K RMS-normalised per (token, head) over the
+  head dimension, q / sqrt(mean(q^2) + 1e-6), with no learned weight;
+* bf16 workloads: every tensor rounded to bf16 (round-to-nearest-even) on the
+  host; the oracle receives exactly those values, upcast to fp64.
+Layout: [batch, tokens, heads, head_dim] (BNHD), tokens row-major over the
+map (t = r*W + c), head_dim contiguous.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+# Attention workloads.  Shapes follow the SDXL / FLUX layers the pages run
+# (PCPP: SDXL on 4-8 devices with p = 0.3 / 0.8; ScaleDiff: SDXL and FLUX at
+# 4096^2 with neighbourhood patch attention).
+ATTENTION_WORKLOADS: Dict[str, dict] = {
+    "pcpp_tiny_fp32": dict(
+        mode="strips", batch=1, heads=2, head_dim=64, map_h=32, map_w=32,
+        num_strips=4, p=0.3, dtype="f32", seed=1001,
+        what="tiny PCPP strips, fp32: 32x32 tokens, 4 strips of 8 rows, p=0.3",
+    ),
+    "sdxl1024_strips": dict(
+        mode="strips", batch=2, heads=10, head_dim=64, map_h=64, map_w=64,
+        num_strips=4, p=0.3, dtype="bf16", seed=1002,
+        what="SDXL 1024^2 mid-level self-attention: 64x64 tokens, 10x64 heads, 4 strips, p=0.3",
+    ),
+    "sdxl2048_strips": dict(
+        mode="strips", batch=2, heads=10, head_dim=64, map_h=128, map_w=128,
+        num_strips=8, p=0.8, dtype="bf16", seed=1003,
+        what="SDXL 2048^2 mid-level self-attention: 128x128 tokens, 10x64 heads, 8 strips, p=0.8",
+    ),
+    "sdxl4096_npa": dict(
+        mode="window", batch=2, heads=10, head_dim=64, map_h=256, map_w=256,
+        tile_h=64, tile_w=64, halo_h=16, halo_w=16, dtype="bf16", seed=1004,
+        what="SDXL 4096^2 first attention level, NPA: 256x256 tokens, 10x64 heads, 64x64 query tiles, 96x96 windows",
+    ),
+    "flux4096_npa": dict(
+        mode="window", batch=1, heads=24, head_dim=128, map_h=256, map_w=256,
+        tile_h=32, tile_w=32, halo_h=16, halo_w=16, dtype="bf16", seed=1005,
+        rms_qk=True,
+        what="FLUX 4096^2 DiT, NPA: 256x256 packed tokens, 24x128 heads, 32x32 query tiles, 64x64 windows",
+    ),
+}
+
+# Structure-guidance blend on the SDXL 4096^2 latent (4 channels, 512x512).
+SG_WORKLOAD = dict(channels=4, map_h=512, map_w=512, w_t=0.5, sigma=4.0, seed=1006,
+                   what="structure-guidance blend: 4x512x512 fp32 latent, sigma=4, w_t=0.5")
+
+STALE_NOISE_STD = 0.05
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returned as fp32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(a), a, out)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of fp32 values that are already bf16-exact."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def attention_inputs(
+    batch: int,
+    heads: int,
+    head_dim: int,
+    map_h: int,
+    map_w: int,
+    *,
+    seed: int,
+    dtype: str = "bf16",
+    stale: bool = True,
+    rms_qk: bool = False,
+    **_ignored,
+) -> Dict[str, Optional[np.ndarray]]:
+    """Draw q, k, v (and k_stale, v_stale) as fp32 arrays of the storage values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (batch, map_h * map_w, heads, head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    k_stale = v_stale = None
+    if stale:
+        k_stale = k + np.float32(STALE_NOISE_STD) * rng.standard_normal(shape, dtype=np.float32)
+        v_stale = v + np.float32(STALE_NOISE_STD) * rng.standard_normal(shape, dtype=np.float32)
+    if rms_qk:
+        for a in (q, k):
+            a /= np.sqrt(np.mean(a.astype(np.float64) ** 2, axis=-1, keepdims=True) + 1e-6).astype(np.float32)
+    out = dict(q=q, k=k, v=v, k_stale=k_stale, v_stale=v_stale)
+    if dtype == "bf16":
+        out = {n: (None if a is None else round_to_bf16(a)) for n, a in out.items()}
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype}")
+    return out
+
+
+def workload_inputs(name: str) -> Dict[str, Optional[np.ndarray]]:
+    w = ATTENTION_WORKLOADS[name]
+    return attention_inputs(**w, stale=(w["mode"] == "strips"))
+
+
+def sg_inputs(channels: int, map_h: int, map_w: int, *, seed: int, batch: int = 1, **_ignored):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((batch, channels, map_h, map_w), dtype=np.float32)
+    ref = rng.standard_normal((batch, channels, map_h, map_w), dtype=np.float32)
+    return x, ref
+
+
+def asg_inputs(shape, *, seed: int):
+    """eps, eps_ref_prev ~ N(0,1); mask ~ U[0,1) (a normalised attention mask stand-in)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    eps = rng.standard_normal(shape, dtype=np.float32)
+    ref = rng.standard_normal(shape, dtype=np.float32)
+    mask = rng.random(shape, dtype=np.float32)
+    return eps, ref, mask
