@@ -1,0 +1,113 @@
+// Structure-guidance kernels.
+//
+// sg_blend: out = x + w * G_sigma * (ref - x), the low-frequency structure
+// guidance of "ScaleDiff ..." (atlas.scime.ai), "Approach", written as one
+// filter of the difference (the filter is linear, so this equals
+// G*ref - G*x).  Separable Gaussian, reflect-101 borders.  Each workgroup
+// produces a 32x64 output tile: the tile plus an R-pixel apron of (ref - x)
+// is staged in LDS, filtered along rows into a second LDS buffer, then along
+// columns straight into the output.  Bandwidth-bound: x and ref are read once
+// from HBM (the apron re-reads hit L2), out is written once.
+//
+// asg_blend: out = eps + w * mask * (eps_ref_prev - eps), element-wise
+// (asynchronous structure guidance, pith.science verdict on ASGDiffusion,
+// "core_discovery").
+#include <hip/hip_runtime.h>
+
+#include "npa_internal.hpp"
+
+namespace npa {
+namespace {
+
+constexpr int kTW = 64, kTH = 32, kThreads = 256;
+
+__device__ __forceinline__ int reflect101(int i, int n) {
+  if (n == 1) return 0;
+  const int period = 2 * (n - 1);
+  i %= period;
+  if (i < 0) i += period;
+  return i < n ? i : period - i;
+}
+
+__global__ __launch_bounds__(kThreads) void sg_blend_kernel(const SgArgs a) {
+  extern __shared__ float smem[];
+  const int R = a.R;
+  const int LW = kTW + 2 * R, LH = kTH + 2 * R;
+  float* diff = smem;           // LH x LW
+  float* tmp = smem + LH * LW;  // LH x kTW
+  const int r0 = blockIdx.y * kTH, c0 = blockIdx.x * kTW;
+  const size_t pb = (size_t)blockIdx.z * a.H * a.W;
+  const float* x = a.x + pb;
+  const float* ref = a.ref + pb;
+
+  for (int i = threadIdx.x; i < LH * LW; i += kThreads) {
+    const int rr = i / LW, cc = i - rr * LW;
+    const int gr = reflect101(r0 - R + rr, a.H), gc = reflect101(c0 - R + cc, a.W);
+    const size_t at = (size_t)gr * a.W + gc;
+    diff[i] = ref[at] - x[at];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < LH * kTW; i += kThreads) {
+    const int rr = i / kTW, cc = i - rr * kTW;
+    const float* src = diff + rr * LW + cc;
+    float acc = 0.0f;
+    for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(a.taps[t], src[t], acc);
+    tmp[i] = acc;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTH * kTW; i += kThreads) {
+    const int rr = i / kTW, cc = i - rr * kTW;
+    const int gr = r0 + rr, gc = c0 + cc;
+    if (gr >= a.H || gc >= a.W) continue;
+    const float* src = tmp + rr * kTW + cc;
+    float acc = 0.0f;
+    for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(a.taps[t], src[t * kTW], acc);
+    const size_t at = (size_t)gr * a.W + gc;
+    a.out[pb + at] = __builtin_fmaf(a.w, acc, x[at]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* __restrict__ eps,
+                                                             const float* __restrict__ ref,
+                                                             const float* __restrict__ mask,
+                                                             float* out, int64_t n4, int64_t count,
+                                                             float w) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+    const f32x4 e = ((const f32x4*)eps)[i];
+    const f32x4 r = ((const f32x4*)ref)[i];
+    const f32x4 m = ((const f32x4*)mask)[i];
+    f32x4 y;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = __builtin_fmaf(w * m[k], r[k] - e[k], e[k]);
+    ((f32x4*)out)[i] = y;
+  }
+  // tail (count % 4 elements) by the first threads of block 0
+  if (blockIdx.x == 0) {
+    const int64_t t = n4 * 4 + threadIdx.x;
+    if (t < count) out[t] = __builtin_fmaf(w * mask[t], ref[t] - eps[t], eps[t]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st) {
+  const dim3 grid((a.W + kTW - 1) / kTW, (a.H + kTH - 1) / kTH, a.planes), block(kThreads);
+  const size_t lds = sizeof(float) * ((size_t)(kTH + 2 * a.R) * (kTW + 2 * a.R) + (size_t)(kTH + 2 * a.R) * kTW);
+  hipLaunchKernelGGL(sg_blend_kernel, grid, block, lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_asg_blend(const float* eps, const float* ref, const float* mask, float* out,
+                            int64_t count, float w, hipStream_t st) {
+  const int64_t n4 = count / 4;
+  int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(asg_blend_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, eps, ref,
+                     mask, out, n4, count, w);
+  return hipGetLastError();
+}
+
+}  // namespace npa

@@ -1,0 +1,116 @@
+// Internal declarations shared by the host API and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "npa.h"
+
+#define NPA_HD __host__ __device__ __forceinline__
+
+namespace npa {
+
+// Validated plan parameters.  Tiles are enumerated in closed form from these,
+// on the host by the planner and on the device by each workgroup, so no tile
+// table ever lives in device memory.
+struct Geo {
+  int32_t mode;      // npa_mode_t
+  int32_t H, W;      // token map
+  int32_t s, h;      // strips: strip height, halo rows
+  int32_t th, tw;    // window: query tile
+  int32_t eh, ew;    // window: halo
+  int32_t tiles_x;   // window: tiles per map row
+  int32_t n_tiles;
+};
+
+// A run of tokens: `rows` runs of `row_len` tokens, first at `start`, `pitch` apart.
+struct Run {
+  int32_t start, row_len, rows, pitch;
+  NPA_HD int32_t count() const { return row_len * rows; }
+};
+
+// The query run of a tile and its key runs (fresh first, then up to two stale).
+struct TileRuns {
+  Run q;
+  Run k[3];
+  int32_t src[3];
+  int32_t nk[3];  // key count per run (0 for an absent run)
+};
+
+NPA_HD int32_t imax(int32_t a, int32_t b) { return a > b ? a : b; }
+NPA_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// Partially conditioned attention (strips): strip i attends to its own rows
+// fresh, plus the h rows nearest to it above and below, stale.
+// Neighbourhood patch attention (window): tile (ti, tj) attends to its window
+// grown by (eh, ew) and clipped at the map border, fresh.
+NPA_HD TileRuns tile_runs(const Geo& g, int32_t tile) {
+  TileRuns t;
+  if (g.mode == NPA_MODE_STRIPS) {
+    const int32_t r0 = tile * g.s, r1 = r0 + g.s;
+    const int32_t a0 = imax(0, r0 - g.h), b1 = imin(g.H, r1 + g.h);
+    t.q = Run{r0 * g.W, g.s * g.W, 1, g.s * g.W};
+    t.k[0] = t.q;
+    t.src[0] = 0;
+    t.k[1] = Run{a0 * g.W, (r0 - a0) * g.W, 1, (r0 - a0) * g.W};
+    t.src[1] = 1;
+    t.k[2] = Run{r1 * g.W, (b1 - r1) * g.W, 1, (b1 - r1) * g.W};
+    t.src[2] = 1;
+  } else {
+    const int32_t ti = tile / g.tiles_x, tj = tile - ti * g.tiles_x;
+    const int32_t r0 = imax(0, ti * g.th - g.eh), r1 = imin(g.H, (ti + 1) * g.th + g.eh);
+    const int32_t c0 = imax(0, tj * g.tw - g.ew), c1 = imin(g.W, (tj + 1) * g.tw + g.ew);
+    t.q = Run{ti * g.th * g.W + tj * g.tw, g.tw, g.th, g.W};
+    t.k[0] = Run{r0 * g.W + c0, c1 - c0, r1 - r0, g.W};
+    t.src[0] = 0;
+    t.k[1] = Run{0, 0, 0, 0};
+    t.src[1] = 1;
+    t.k[2] = Run{0, 0, 0, 0};
+    t.src[2] = 1;
+  }
+  for (int i = 0; i < 3; ++i) t.nk[i] = t.k[i].count();
+  return t;
+}
+
+NPA_HD int32_t tile_queries(const Geo& g) {
+  return g.mode == NPA_MODE_STRIPS ? g.s * g.W : g.th * g.tw;
+}
+
+// Arguments of the attention kernels (passed by value).
+struct AttnArgs {
+  const void* q;
+  const void* kf;
+  const void* vf;
+  const void* ks;
+  const void* vs;
+  void* o;
+  int64_t sb, sn, sh;  // strides in elements
+  int32_t B, Hh;
+  Geo g;
+  int32_t qblocks;  // query blocks per tile
+  int32_t nblocks;  // grid size
+  float scale;      // softmax scale
+  float c;          // scale * log2(e)
+};
+
+// Arguments of the structure-guidance kernel.
+constexpr int kSgMaxRadius = 24;  // sigma <= 8; keeps the LDS tile under 64 KiB
+struct SgArgs {
+  const float* x;
+  const float* ref;
+  float* out;
+  int32_t planes, H, W, R;
+  float w;
+  float taps[2 * kSgMaxRadius + 1];
+};
+
+// Launchers (return the HIP error of the launch).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int block_m, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int block_m, hipStream_t st);
+int attn_bf16_block_m(int head_dim);  // queries per workgroup, 0 if unsupported
+int attn_f32_block_m(int head_dim);
+hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st);
+hipError_t launch_asg_blend(const float* eps, const float* ref, const float* mask, float* out,
+                            int64_t count, float w, hipStream_t st);
+
+}  // namespace npa

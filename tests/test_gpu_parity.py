@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+* small ragged maps, every output compared (bf16 atol 2e-2, fp32 atol 1e-4);
+* the five attention workloads at full size, in the launch configuration the
+  benchmark times, on sampled query tiles that the oracle computes exactly;
+* structural probes: Q = 0 set means, one-hot V exposing probability rows,
+  NaN poisoning of everything the plan must not read;
+* the structure-guidance and asynchronous-guidance blends.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import guidance as G
+from partial_context_patch_amd import npa
+from partial_context_patch_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+ATOL = {"bf16": 2e-2, "f32": 1e-4}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _dev(a, dt):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(TDT[dt])
+
+
+def _kw(spec):
+    if isinstance(spec, A.Strips):
+        return dict(strips=spec.num_strips, p=spec.p, halo_rows=spec.halo_rows)
+    return dict(tile=(spec.tile_h, spec.tile_w), halo=(spec.halo_h, spec.halo_w))
+
+
+def _run(inp, H, W, spec, dt, scale=None):
+    q, k, v = (_dev(inp[n], dt) for n in ("q", "k", "v"))
+    ks, vs = _dev(inp.get("k_stale"), dt), _dev(inp.get("v_stale"), dt)
+    out = npa.attn_fwd(q, k, v, ks, vs, map_hw=(H, W), scale=scale, **_kw(spec))
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    # (H, W, B, Hh, d, spec, dtype)
+    (24, 20, 1, 2, 64, A.Strips(3, halo_rows=3), "bf16"),
+    (24, 20, 2, 3, 64, A.Strips(3, p=0.3), "bf16"),
+    (30, 13, 1, 2, 64, A.Strips(5, halo_rows=9), "bf16"),
+    (16, 24, 1, 2, 64, A.Strips(1, p=0.5), "bf16"),
+    (16, 24, 1, 2, 128, A.Strips(4, p=0.5), "bf16"),
+    (40, 36, 1, 2, 64, A.Windows(8, 12, 5, 3), "bf16"),
+    (40, 36, 2, 2, 128, A.Windows(20, 12, 4, 7), "bf16"),
+    (24, 24, 1, 1, 64, A.Windows(24, 24, 0, 0), "bf16"),
+    (12, 10, 1, 2, 64, A.Windows(1, 2, 1, 3), "bf16"),
+    (24, 20, 1, 2, 64, A.Strips(3, halo_rows=3), "f32"),
+    (24, 20, 1, 2, 32, A.Strips(4, halo_rows=2), "f32"),
+    (40, 36, 1, 2, 128, A.Windows(8, 12, 5, 3), "f32"),
+]
+
+
+@pytest.mark.parametrize("H,W,B,Hh,d,spec,dt", SMALL)
+def test_small_ragged_full_compare(H, W, B, Hh, d, spec, dt):
+    stale = isinstance(spec, A.Strips)
+    inp = WL.attention_inputs(B, Hh, d, H, W, seed=7 + H + W + d, dtype=dt, stale=stale)
+    got = _run(inp, H, W, spec, dt)
+    ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec)
+    err = np.abs(got - ref).max()
+    assert np.isfinite(got).all()
+    assert err <= ATOL[dt], f"max abs err {err}"
+
+
+def test_explicit_scale_and_halo_beyond_map():
+    H, W = 16, 16
+    inp = WL.attention_inputs(1, 2, 64, H, W, seed=5, dtype="bf16")
+    spec = A.Strips(4, halo_rows=40)  # every other strip entirely stale
+    got = _run(inp, H, W, spec, "bf16", scale=0.2)
+    ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec, scale=0.2)
+    assert np.abs(got - ref).max() <= 2e-2
+
+
+# ------------------------------------------------------------- full sizes
+def _workload_spec(w):
+    if w["mode"] == "strips":
+        return A.Strips(w["num_strips"], p=w["p"])
+    return A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
+
+
+def _sample_queries(w, spec):
+    """Every query of a corner, an edge and an interior tile (windows), or the
+    first, middle and last rows of every strip."""
+    H, W = w["map_h"], w["map_w"]
+    tiles = list(A.iter_tiles(H, W, spec))
+    if isinstance(spec, A.Strips):
+        s = H // spec.num_strips
+        rows = sorted({r for i in range(spec.num_strips) for r in (i * s, i * s + s // 2, i * s + s - 1)})
+        return np.concatenate([np.arange(r * W, (r + 1) * W) for r in rows])
+    tx = W // spec.tile_w
+    ty = H // spec.tile_h
+    pick = [0, tx // 2, (ty // 2) * tx + tx // 2, ty * tx - 1]
+    return np.concatenate([tiles[i][0] for i in sorted(set(pick))])
+
+
+@pytest.mark.parametrize("name", list(WL.ATTENTION_WORKLOADS))
+def test_workload_full_size_sampled(name):
+    w = WL.ATTENTION_WORKLOADS[name]
+    print(f"[parity] workload {name}: {w['what']}", flush=True)
+    inp = WL.workload_inputs(name)
+    spec = _workload_spec(w)
+    got = _run(inp, w["map_h"], w["map_w"], spec, w["dtype"])
+    assert np.isfinite(got).all()
+    qs = _sample_queries(w, spec)
+    heads = [(0, 0), (w["batch"] - 1, w["heads"] - 1)]
+    ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], w["map_h"], w["map_w"],
+                            spec, query_tokens=qs, heads=heads)
+    for b, j in heads:
+        err = np.abs(got[b, qs, j] - ref[b, qs, j]).max()
+        assert err <= ATOL[w["dtype"]], f"{name} (b={b}, head={j}): max abs err {err}"
+
+
+# ----------------------------------------------------------- structural
+@pytest.mark.parametrize("spec", [A.Strips(2, halo_rows=1), A.Strips(4, halo_rows=2), A.Strips(4, halo_rows=0),
+                                  A.Windows(2, 2, 1, 1), A.Windows(1, 4, 2, 0)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_one_hot_values_expose_probability_rows(spec, dt):
+    """4x4 map, d = 64: V_fresh = [I16|0|0], V_stale = [0|I16|0], so out[:, :32]
+    is the probability row over the 32 candidate keys."""
+    H = W = 4
+    N = 16
+    rng = np.random.Generator(np.random.PCG64(3))
+    q = rng.standard_normal((1, N, 1, 64), dtype=np.float32)
+    k = rng.standard_normal((1, N, 1, 64), dtype=np.float32)
+    ks = rng.standard_normal((1, N, 1, 64), dtype=np.float32)
+    if dt == "bf16":
+        q, k, ks = (WL.round_to_bf16(a) for a in (q, k, ks))
+    vf = np.zeros((1, N, 1, 64), np.float32)
+    vs = np.zeros((1, N, 1, 64), np.float32)
+    vf[0, :, 0, :N] = np.eye(N)
+    vs[0, :, 0, N:2 * N] = np.eye(N)
+    got = _run(dict(q=q, k=k, v=vf, k_stale=ks, v_stale=vs), H, W, spec, dt)[0, :, 0, :]
+    P = got[:, :2 * N]
+    ref = A.attention_tier1(q, k, vf, ks, vs, H, W, spec)[0, :, 0, :2 * N]
+    sets = A.attended_sets(H, W, spec)
+    for t in range(N):
+        allowed = np.zeros(2 * N, dtype=bool)
+        allowed[sets[t][0]] = True
+        allowed[[N + u for u in sets[t][1]]] = True
+        assert np.all(P[t, ~allowed] == 0.0), f"query {t} weighs keys outside its set"
+        assert np.all(P[t, allowed] > 0.0), f"query {t} misses keys of its set"
+    assert np.abs(got[:, 2 * N:]).max() == 0.0
+    tol = 1e-2 if dt == "bf16" else 1e-5
+    np.testing.assert_allclose(P.sum(1), 1.0, atol=tol)
+    np.testing.assert_allclose(P, ref, atol=tol)
+
+
+@pytest.mark.parametrize(
+    "H,W,spec",
+    [(16, 16, A.Strips(4, halo_rows=3)), (32, 8, A.Strips(8, halo_rows=5)), (16, 16, A.Strips(2, halo_rows=16)),
+     (16, 16, A.Windows(4, 8, 3, 2)), (24, 24, A.Windows(8, 8, 5, 5))],
+)
+def test_zero_query_set_means(H, W, spec):
+    """Q = 0 gives uniform weights: out = mean of V over the attended set, with
+    V = (1, is_stale, row/H, col/W): set size ratio and mean row/col in closed form."""
+    N = H * W
+    rows, cols = np.arange(N) // W, np.arange(N) % W
+    d = 64
+    q = np.zeros((1, N, 1, d), np.float32)
+    k = np.random.Generator(np.random.PCG64(4)).standard_normal((1, N, 1, d), dtype=np.float32)
+    k = WL.round_to_bf16(k)
+    vf = np.zeros((1, N, 1, d), np.float32)
+    vs = np.zeros((1, N, 1, d), np.float32)
+    vf[0, :, 0, 0] = 1.0
+    vs[0, :, 0, 0] = 1.0
+    vs[0, :, 0, 1] = 1.0
+    for v in (vf, vs):
+        v[0, :, 0, 2] = rows / 64.0  # exact in bf16
+        v[0, :, 0, 3] = cols / 64.0
+    got = _run(dict(q=q, k=k, v=vf, k_stale=k, v_stale=vs), H, W, spec, "bf16")[0, :, 0]
+    sets = A.attended_sets(H, W, spec)
+    for t in range(N):
+        fr, st = sets[t]
+        n = len(fr) + len(st)
+        assert got[t, 0] == pytest.approx(1.0, abs=8e-3)
+        assert got[t, 1] == pytest.approx(len(st) / n, abs=8e-3)
+        assert got[t, 2] == pytest.approx((rows[fr].sum() + rows[st].sum()) / n / 64.0, abs=4e-3)
+        assert got[t, 3] == pytest.approx((cols[fr].sum() + cols[st].sum()) / n / 64.0, abs=4e-3)
+
+
+@pytest.mark.parametrize(
+    "H,W,spec,d",
+    [(32, 32, A.Strips(4, halo_rows=3), 64), (48, 16, A.Strips(3, halo_rows=5), 128),
+     (40, 36, A.Windows(8, 12, 5, 3), 64), (32, 32, A.Windows(16, 16, 4, 4), 128)],
+)
+def test_nan_poisoned_unread_regions(H, W, spec, d):
+    """Fill everything the definition never reads with NaN; the result must be
+    finite and equal to the clean run.  Stale copies of a strip's own rows and
+    stale rows beyond the halo are poisoned; for one tile, every fresh key
+    outside its set is poisoned and only that tile's outputs are checked."""
+    inp = WL.attention_inputs(1, 2, d, H, W, seed=11, dtype="bf16", stale=True)
+    clean = _run(inp, H, W, spec, "bf16")
+    tiles = list(A.iter_tiles(H, W, spec))
+    used_stale = np.zeros(H * W, dtype=bool)
+    for _, _, st in tiles:
+        used_stale[st] = True
+    pois = dict(inp)
+    for n in ("k_stale", "v_stale"):
+        a = pois[n].copy()
+        a[:, ~used_stale] = np.nan
+        pois[n] = a
+    qt, ft, st = tiles[len(tiles) // 2]
+    keep = np.zeros(H * W, dtype=bool)
+    keep[ft] = True
+    for n in ("k", "v"):
+        a = pois[n].copy()
+        a[:, ~keep & ~np.isin(np.arange(H * W), qt)] = np.nan
+        pois[n] = a
+    for n in ("k_stale", "v_stale"):
+        a = pois[n].copy()
+        other = np.ones(H * W, dtype=bool)
+        other[st] = False
+        a[:, other] = np.nan
+        pois[n] = a
+    got = _run(pois, H, W, spec, "bf16")
+    assert np.isfinite(got[:, qt]).all()
+    np.testing.assert_array_equal(got[:, qt], clean[:, qt])
+
+
+# ------------------------------------------------------------- guidance
+@pytest.mark.parametrize(
+    "shape,sigma,w",
+    [((1, 4, 512, 512), 4.0, 0.5), ((2, 3, 37, 70), 4.0, 0.8), ((1, 1, 5, 9), 4.0, 1.0),
+     ((1, 2, 64, 33), 1.5, -0.3), ((1, 1, 100, 130), 8.0, 0.5)],
+)
+def test_sg_blend(shape, sigma, w):
+    seed = sum(shape)
+    x, ref = WL.sg_inputs(shape[1], shape[2], shape[3], seed=seed, batch=shape[0])
+    out = npa.sg_blend(torch.from_numpy(x).cuda(), torch.from_numpy(ref).cuda(), w, sigma)
+    torch.cuda.synchronize()
+    exp = G.sg_blend(x, ref, w, sigma)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - exp).max()
+    assert err <= 1e-5, f"max abs err {err}"
+
+
+def test_sg_blend_workload_is_lfm_at_w1():
+    w = WL.SG_WORKLOAD
+    x, ref = WL.sg_inputs(w["channels"], w["map_h"], w["map_w"], seed=w["seed"])
+    out = npa.sg_blend(torch.from_numpy(x).cuda(), torch.from_numpy(ref).cuda(), 1.0, w["sigma"])
+    torch.cuda.synchronize()
+    # latent frequency mixing: low frequencies of ref plus high frequencies of x
+    lfm = G.lowpass(ref, w["sigma"]) + (x - G.lowpass(x, w["sigma"]))
+    assert np.abs(out.cpu().numpy() - lfm).max() <= 1e-5
+
+
+@pytest.mark.parametrize("count", [1, 3, 4, 1000, 1 << 20, (1 << 20) + 3])
+def test_asg_blend(count):
+    eps, ref, mask = WL.asg_inputs((count,), seed=count)
+    out = npa.asg_blend(*(torch.from_numpy(a).cuda() for a in (eps, ref, mask)), 0.7)
+    torch.cuda.synchronize()
+    exp = G.asg_blend(eps, ref, mask, 0.7)
+    assert np.abs(out.cpu().numpy() - exp).max() <= 1e-6
