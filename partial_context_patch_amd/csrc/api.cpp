@@ -197,7 +197,13 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   for (const void* p : ins)
     if (overlaps(out, p, L, esize)) return fail(NPA_ERR_INVALID_ARG, "out must not alias an input");
 
+  const int64_t range = ((int64_t)L->map_h * L->map_w - 1) * L->stride_n * esize + (int64_t)L->head_dim * esize;
+  if (L->dtype == NPA_BF16 && range > 0x7FFFFFF0ll)
+    return fail(NPA_ERR_UNSUPPORTED,
+                "one (batch, head) slice spans %lld bytes; the bf16 kernel addresses at most 2^31-16",
+                (long long)range);
   npa::AttnArgs a;
+  a.range_bytes = (uint32_t)(range > 0xFFFFFFFFll ? 0xFFFFFFFFll : range);
   a.q = Q;
   a.kf = K_fresh;
   a.vf = V_fresh;

@@ -8,21 +8,34 @@
 // score matrix never leaves registers and K/V are read in place from the
 // fresh and stale buffers (never concatenated).
 //
-// Workgroup = 4 waves; each wave owns ROWS = 32*NT queries of one tile, and
-// the workgroup walks the tile's keys in blocks of 64, staged through a
-// double-buffered LDS tile (one barrier per block).
+// Workgroup = 4 waves; each wave owns ROWS = 32*NT queries of one tile.  The
+// workgroup walks the tile's keys in blocks of 64 staged through a
+// double-buffered LDS tile (one barrier per block); each wave consumes a block
+// as two 32-key sub-blocks.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, lane l: column l%32, half g=l/32):
 //   S^T = K * Q^T   A = K rows (keys),  B = Q^T (queries in columns)
 //   O^T = V^T * P^T A = V^T (head dims), B = P^T
-// With scores transposed, each lane holds 32 keys of ONE query, so the row max
-// and row sum are in-lane reductions plus one exchange with lane l^32
-// (v_permlane32_swap), and rescaling O^T by a per-query factor is in-lane.
-// K rows are loaded in the order pi(r) = r with bits 2 and 3 swapped, which
-// makes the accumulator entries j=0..7 of lane half g hold keys 8g..8g+7 --
-// exactly the B-operand layout the PV product needs, so P goes from the score
-// accumulator to the MFMA operand without any lane movement.  V^T fragments
-// come from the row-major V tile through ds_read_b64_tr_b16.
+// With scores transposed, each lane holds 16 keys of ONE query per sub-block:
+// row reductions are in-lane plus one v_permlane32_swap, and rescaling O^T by
+// a per-query factor is in-lane.  K rows are loaded in the order
+// pi(r) = r with bits 2 and 3 swapped, which puts accumulator entries j=0..7 of
+// lane half g on keys 8g..8g+7 -- the B-operand layout of the PV product -- so P
+// goes from the score accumulator to the MFMA operand with no lane movement.
+// V^T fragments come from the row-major V tile through ds_read_b64_tr_b16.
+//
+// Softmax arithmetic is kept off the VALU wherever the MFMA can carry it:
+//   * Q is multiplied by scale*log2(e) once at load (re-rounded to bf16), so
+//     the product is already in the exp2 domain;
+//   * the running shift -m enters as the C operand of the first S^T MFMA
+//     (a persistent register tile), so p = exp2(acc) with no subtraction;
+//   * the shift is the exact row max of the first 32 keys and is raised only
+//     when a row sum would exceed 2^60 (checked from the sum itself), so the
+//     common path has no max, no rescale of O and no branch per query;
+//   * row sums come from v_dot2c_f32_bf16 on the packed bf16 P, i.e. the
+//     denominator sums exactly the weights the numerator uses.
+// Loads and stores go through buffer descriptors: out-of-range keys and
+// queries read zeros / drop their stores without branches.
 #include <hip/hip_runtime.h>
 
 #include "npa_internal.hpp"
@@ -32,15 +45,20 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;  // keys per block
+constexpr int kBN = 64;                  // keys per LDS block
+constexpr uint32_t kOOB = 0x7FFFFFF0u;   // byte offset past every buffer's range
+constexpr float kOverflow = 1.152921504606846976e18f;  // 2^60
 
 template <int D>
 struct Cfg;
@@ -84,6 +102,20 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16-byte chunk permutation of LDS row r.  With it, the 8 lanes of each
+// ds_read_b128 quarter (K fragments: rows {0..3, 8..11} + 4k, one chunk) and
+// the 16 lanes of each ds_read_b64_tr_b16 quarter (V fragments: 4 consecutive
+// rows x 2 adjacent chunks) hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Token of the j-th key of the tile and which buffer (0 fresh, 1 stale) holds it.
 template <int MODE>
 __device__ __forceinline__ int key_token(const TileRuns& t, int j, float inv_len, int& src) {
@@ -103,22 +135,73 @@ __device__ __forceinline__ int key_token(const TileRuns& t, int j, float inv_len
   }
 }
 
+// exp2 of 16 accumulator entries, packed to bf16 pairs for the PV operand;
+// returns the sum of the packed (bf16) weights.
+__device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8& p0, bf16x8& p1) {
+  f32x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = __builtin_amdgcn_exp2f(acc[i] - shift);
+    b[i] = __builtin_amdgcn_exp2f(acc[8 + i] - shift);
+  }
+  p0 = __builtin_convertvector(a, bf16x8);
+  p1 = __builtin_convertvector(b, bf16x8);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * i], p1[2 * i + 1]}, one, s, false);
+  }
+  return s;
+}
+
+// Same without a shift argument (the common path: the shift is inside acc).
+__device__ __forceinline__ float exp_pack0(const f32x16& acc, bf16x8& p0, bf16x8& p1) {
+  f32x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = __builtin_amdgcn_exp2f(acc[i]);
+    b[i] = __builtin_amdgcn_exp2f(acc[8 + i]);
+  }
+  p0 = __builtin_convertvector(a, bf16x8);
+  p1 = __builtin_convertvector(b, bf16x8);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * i], p1[2 * i + 1]}, one, s, false);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float m = fmaxf(a[0], a[1]);
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(a[i], a[i + 1]));
+  return m;
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int NT = Cfg<D>::NT;
   constexpr int ROWS = 32 * NT;
   constexpr int BM = kWaves * ROWS;
-  constexpr int MT = kBN / 32;  // 32-key tiles per block
   constexpr int KS = D / 16;    // k-steps of S^T
   constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
-  constexpr int PK = kBN / 16;  // k-steps of O^T
-  constexpr int LDR = D + 8;    // LDS row pitch in elements (16-byte pad)
+  constexpr int LDR = D;        // LDS row pitch in elements (unpadded; chunks XOR-swizzled)
   constexpr int CPR = D / 8;    // 16-byte chunks per key row
-  constexpr int CH = kBN * CPR / kThreads;
+  constexpr int CH = kBN * CPR / kThreads;  // DMA instructions per thread per tile
   static_assert(CH * kThreads == kBN * CPR, "chunking");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][kBN * LDR];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][kBN * LDR];
+  // Two K and two V tiles as four separate objects: the copy into one tile is
+  // then provably disjoint from the reads of the other, so waiting for it is
+  // left to the explicit wait before each barrier.
+  __shared__ __attribute__((aligned(16))) __bf16 sk0[kBN * LDR];
+  __shared__ __attribute__((aligned(16))) __bf16 sk1[kBN * LDR];
+  __shared__ __attribute__((aligned(16))) __bf16 sv0[kBN * LDR];
+  __shared__ __attribute__((aligned(16))) __bf16 sv1[kBN * LDR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -137,183 +220,231 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   const int64_t bh = (int64_t)b * a.sb + (int64_t)head * a.sh;
   const float inv_qlen = 1.0f / (float)tr.q.row_len;
   const float inv_klen = 1.0f / (float)tr.k[0].row_len;
+  const uint32_t sn2 = (uint32_t)a.sn * 2u;  // token stride in bytes
 
-  const __bf16* qp = (const __bf16*)a.q;
-  const __bf16* kfp = (const __bf16*)a.kf;
-  const __bf16* vfp = (const __bf16*)a.vf;
-  const __bf16* ksp = (const __bf16*)a.ks;
-  const __bf16* vsp = (const __bf16*)a.vs;
+  const rsrc_t rq = make_rsrc((const __bf16*)a.q + bh, a.range_bytes);
+  const rsrc_t rkf = make_rsrc((const __bf16*)a.kf + bh, a.range_bytes);
+  const rsrc_t rvf = make_rsrc((const __bf16*)a.vf + bh, a.range_bytes);
+  const rsrc_t rks = make_rsrc((const __bf16*)a.ks + bh, a.range_bytes);
+  const rsrc_t rvs = make_rsrc((const __bf16*)a.vs + bh, a.range_bytes);
+  const rsrc_t ro = make_rsrc((__bf16*)a.o + bh, a.range_bytes);
 
-  // ---- Q^T fragments: lane (query l32, half g) holds dims 16*ks + 8g .. +8
+  // ---- Q^T fragments, pre-multiplied by scale*log2(e):
+  //      lane (query l32, half g) holds dims 16*ks + 8g .. +8
   bf16x8 qf[NT][KS];
-  int64_t qoff[NT];
-  bool qok[NT];
+  uint32_t qoff[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int qi = qb * BM + wave * ROWS + nt * 32 + l32;
-    qok[nt] = qi < nq;
-    int tok = 0;
-    if (qok[nt]) {
+    uint32_t off = kOOB;
+    if (qi < nq) {
+      int tok;
       if (MODE == NPA_MODE_STRIPS) {
         tok = tr.q.start + qi;
       } else {
         const int r = fast_div(qi, tr.q.row_len, inv_qlen);
         tok = tr.q.start + r * tr.q.pitch + (qi - r * tr.q.row_len);
       }
+      off = (uint32_t)tok * sn2;
     }
-    qoff[nt] = bh + (int64_t)tok * a.sn;
+    qoff[nt] = off;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qok[nt]) v = *(const u32x4*)(qp + qoff[nt] + ks * 16 + g * 8);
-      qf[nt][ks] = __builtin_bit_cast(bf16x8, v);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32 + g * 16, 0, 0);
+      f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] *= a.c;
+      qf[nt][ks] = __builtin_convertvector(f, bf16x8);
     }
   }
 
-  // ---- K/V staging registers
-  u32x4 kr[CH], vr[CH];
-  auto fetch = [&](int kb) {
+  // ---- K/V tiles go from HBM straight into LDS (buffer_load ... lds): one
+  // instruction fills 1 KiB, lane L's 16 bytes landing at byte 16*L.  Each lane
+  // picks the global chunk that belongs at its slot, so the tile is stored
+  // row-major with the 16-byte chunks of row r XOR-permuted by swz(r); keys past
+  // the end of the set read zeros (out-of-range offset).
+  auto fetch = [&](int kb, __bf16* skd, __bf16* svd) {
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      const int c = tid + r * kThreads;
-      const int key = c / CPR, dc = c % CPR;
-      const int kidx = kb * kBN + key;
-      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (kidx < nk) {
-        int src;
-        const int tok = key_token<MODE>(tr, kidx, inv_klen, src);
-        const int64_t off = bh + (int64_t)tok * a.sn + dc * 8;
-        kk = *(const u32x4*)((src ? ksp : kfp) + off);
-        vv = *(const u32x4*)((src ? vsp : vfp) + off);
+      const int inst = wave * CH + r;
+      const int pos = inst * 64 + lane;  // chunk slot in the tile
+      const int row = pos / CPR, slot = pos % CPR;
+      const int kidx = kb * kBN + row;
+      int src = 0;
+      uint32_t off = kOOB;
+      if (kidx < nk) off = (uint32_t)key_token<MODE>(tr, kidx, inv_klen, src) * sn2 + (slot ^ swz(row)) * 16;
+      lds_ptr dk = (lds_ptr)&skd[inst * 512];
+      lds_ptr dv = (lds_ptr)&svd[inst * 512];
+      if (MODE == NPA_MODE_STRIPS && src) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, dk, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, dv, 16, off, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkf, dk, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvf, dv, 16, off, 0, 0, 0);
       }
-      kr[r] = kk;
-      vr[r] = vv;
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int c = tid + r * kThreads;
-      const int key = c / CPR, dc = c % CPR;
-      *(u32x4*)&sk[buf][key * LDR + dc * 8] = kr[r];
-      *(u32x4*)&sv[buf][key * LDR + dc * 8] = vr[r];
     }
   };
 
   f32x16 o[DT][NT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[dt][nt] = f32x16{};
-  float m[NT], l[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m[nt] = -INFINITY;
-    l[nt] = 0.0f;
-  }
+  float nm[NT];  // -m: broadcast into the C operand of the first S^T MFMA
+  float l[NT];
 
   // row of the K tile this lane feeds into the S^T product: bits 2,3 of l32 swapped
   const int krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   // ds_read_b64_tr_b16 source address pattern for the V^T fragments
   const int vkey = 8 * g + ((lane & 15) >> 2);
   const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const float c = a.c;
-
   const int nkb = (nk + kBN - 1) / kBN;
-  fetch(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    stage(buf);
-    __syncthreads();
-    if (kb + 1 < nkb) fetch(kb + 1);
 
-    // ---- S^T = K Q^T
-    f32x16 s[MT][NT];
+  // Exact row max of the whole tile (the rare second pass only): S^T with a
+  // zero shift, reduced over every key.
+  auto row_max = [&](float (&mx)[NT]) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
+    auto block = [&](int kb, const __bf16* skb, __bf16* skn, __bf16* svn) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[mt][nt] = f32x16{};
-    const __bf16* skb = sk[buf];
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 s[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+        for (int ks = 0; ks < KS; ++ks) {
+          const int row = mt * 32 + krow;
+          const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)&skb[(mt * 32 + krow) * LDR + ks * 16 + g * 8];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma(kf, qf[nt][ks], s[mt][nt]);
-      }
-    }
-
-    // ---- mask keys past the end of the tile's key set (last block only)
-    if (kb * kBN + kBN > nk) {
-      const int base = nk - kb * kBN;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kl = 32 * mt + (j < 8 ? 8 * g + j : 16 + 8 * g + (j - 8));
-          if (kl >= base)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) s[mt][nt][j] = -INFINITY;
+          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? f32x16{} : s[nt]);
         }
+        const int base = nk - kb * kBN - mt * 32;
+        const int t = base - 8 * g;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if ((j < 8 ? j : j + 8) < t)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) mx[nt] = fmaxf(mx[nt], s[nt][j]);
+      }
+    };
+    fetch(0, sk0, sv0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      block(kb, sk0, sk1, sv1);
+      if (kb + 1 < nkb) block(kb + 1, sk1, sk0, sv0);
     }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = pair_max(mx[nt]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // the tiles are free again
+  };
 
-    // ---- online softmax (exp2 domain); P packed straight into PV operands
-    bf16x8 pf[NT][PK];
+  // One pass over the tile's keys with a fixed shift: p = exp2(acc), no max and
+  // no rescale inside the loop.  preset=false: the shift is the exact row max
+  // of the first 32 keys.  preset=true: the shift was set beforehand (the true
+  // row max of the tile).
+  auto pass = [&](bool preset) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = s[0][nt][0];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x16{};
+      l[nt] = 0.0f;
+    }
+    auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn) {
+      // this wave's copies into tile kb are done; after the barrier, everyone's are
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[mt][nt][j]);
-      mx = pair_max(mx);
-      const float mn = fmaxf(m[nt], mx);
-      const float alpha = __builtin_amdgcn_exp2f((m[nt] - mn) * c);
-      const float mc = mn * c;
-      float rs = 0.0f;
+      for (int mt = 0; mt < 2; ++mt) {
+        // ---- S^T (already in the exp2 domain, already shifted by -m)
+        f32x16 s[NT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int ks = 0; ks < KS; ++ks) {
+          const int row = mt * 32 + krow;
+          const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          f32x8 pv;
+          for (int nt = 0; nt < NT; ++nt) {
+            f32x16 c0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][nt][8 * h2 + i], c, -mc));
-            rs += p;
-            pv[i] = p;
+            for (int j = 0; j < 16; ++j) c0[j] = nm[nt];
+            s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? c0 : s[nt]);
           }
-          pf[nt][2 * mt + h2] = __builtin_convertvector(pv, bf16x8);
+        }
+        // ---- keys past the end of the tile's set (last block only):
+        // entry j of lane half g is key 8g + j (j < 8) or 8g + j + 8 (j >= 8)
+        const int base = nk - kb * kBN - mt * 32;
+        if (base < 32) {
+          const int t = base - 8 * g;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if ((j < 8 ? j : j + 8) >= t)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) s[nt][j] = -INFINITY;
+          }
+        }
+        // ---- weights
+        bf16x8 p0[NT], p1[NT];
+        if (kb == 0 && mt == 0 && !preset) {
+          // first sub-block: its exact row max becomes the shift
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float m = pair_max(max16(s[nt]));
+            l[nt] = exp_pack(s[nt], m, p0[nt], p1[nt]);
+            nm[nt] = -m;
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s[nt], p0[nt], p1[nt]);
+        }
+        // ---- O^T += V^T P^T over the sub-block's 32 keys
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int r0 = mt * 32 + 16 * h2 + vkey, r1 = r0 + 4;
+            const int col = 32 * dt + vdim;  // multiple of 4: one 8-byte half of a chunk
+            const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
+            const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
+            const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma(vf, h2 ? p1[nt] : p0[nt], o[dt][nt]);
+          }
         }
       }
-      l[nt] = l[nt] * alpha + rs;
-      m[nt] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][nt] *= alpha;
+    };
+    fetch(0, sk0, sv0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      block(kb, sk0, sv0, sk1, sv1);
+      if (kb + 1 < nkb) block(kb + 1, sk1, sv1, sk0, sv0);
     }
+  };
 
-    // ---- O^T += V^T P^T
-    const __bf16* svb = sv[buf];
+  // The fast pass is kept unless some row sum leaves [1, 2^60] -- a later key
+  // beating the first keys' max by ~60 in log2 units, or a non-finite input.
+  // Then the workgroup computes every row's true max and runs the pass again
+  // with that shift, where every weight is <= 1 and the max itself weighs 1.
+  __shared__ int redo;
+  if (tid == 0) redo = 0;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+  for (int nt = 0; nt < NT; ++nt) nm[nt] = 0.0f;
+  pass(false);
+  bool bad = false;
 #pragma unroll
-      for (int kk = 0; kk < PK; ++kk) {
-        const __bf16* p0 = &svb[(16 * kk + vkey) * LDR + 32 * dt + vdim];
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0);
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0 + 4 * LDR));
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  for (int nt = 0; nt < NT; ++nt) bad |= !(pair_sum(l[nt]) <= kOverflow);
+  if (wave_any(bad) && lane == 0) redo = 1;  // every writer stores 1
+  __syncthreads();
+  if (redo) {
+    float mx[NT];
+    row_max(mx);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma(vf, pf[nt][kk], o[dt][nt]);
-      }
-    }
+    for (int nt = 0; nt < NT; ++nt) nm[nt] = -mx[nt];
+    pass(true);
   }
 
   // ---- normalise and store: lane (query, g) holds dims 32dt + 8*j4 + 4g .. +4
-  __bf16* op = (__bf16*)a.o;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float inv = 1.0f / pair_sum(l[nt]);
-    if (!qok[nt]) continue;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -321,7 +452,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = o[dt][nt][4 * j4 + i] * inv;
-        *(bf16x4*)(op + qoff[nt] + 32 * dt + 8 * j4 + 4 * g) = __builtin_convertvector(v, bf16x4);
+        const bf16x4 h = __builtin_convertvector(v, bf16x4);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), ro,
+                                              qoff[nt] + (32 * dt + 8 * j4 + 4 * g) * 2, 0, 0);
       }
   }
 }

@@ -91,6 +91,7 @@ struct AttnArgs {
   int32_t nblocks;  // grid size
   float scale;      // softmax scale
   float c;          // scale * log2(e)
+  uint32_t range_bytes;  // bytes spanned by one (batch, head) slice: ((N-1)*sn + d) * esize
 };
 
 // Arguments of the structure-guidance kernel.

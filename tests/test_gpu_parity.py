@@ -258,3 +258,26 @@ def test_asg_blend(count):
     torch.cuda.synchronize()
     exp = G.asg_blend(eps, ref, mask, 0.7)
     assert np.abs(out.cpu().numpy() - exp).max() <= 1e-6
+
+
+@pytest.mark.parametrize("spec,H,W,d", [(A.Windows(8, 8, 4, 4), 16, 16, 64), (A.Strips(2, halo_rows=3), 16, 16, 64),
+                                        (A.Windows(8, 8, 4, 4), 16, 16, 128)])
+def test_late_large_logits_take_the_robust_pass(spec, H, W, d):
+    """Keys far beyond the first 32 of a tile score ~100+ log2 units above them:
+    the fixed-shift pass overflows, the workgroup must redo the tile with the
+    tile's true row max.  Also rows whose logits are all hugely negative."""
+    N = H * W
+    rng = np.random.Generator(np.random.PCG64(21))
+    q = 0.05 * rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    k = 0.05 * rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    v = rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    q[0, :, 0, 0] = 24.0           # head 0: a few late keys align with every query
+    k[0, N - 5:, 0, 0] = 24.0
+    q[0, :, 1, 0] = -40.0          # head 1: every logit very negative, spread by k
+    k[0, :, 1, 0] = rng.uniform(20.0, 40.0, N).astype(np.float32)
+    q, k, v = (WL.round_to_bf16(a) for a in (q, k, v))
+    inp = dict(q=q, k=k, v=v, k_stale=k.copy(), v_stale=v.copy())
+    got = _run(inp, H, W, spec, "bf16")
+    ref = A.attention_tier1(q, k, v, inp["k_stale"], inp["v_stale"], H, W, spec)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= 2e-2
