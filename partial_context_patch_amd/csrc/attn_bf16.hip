@@ -49,6 +49,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -116,23 +117,49 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Token of the j-th key of the tile and which buffer (0 fresh, 1 stale) holds it.
-template <int MODE>
-__device__ __forceinline__ int key_token(const TileRuns& t, int j, float inv_len, int& src) {
-  if (MODE == NPA_MODE_STRIPS) {
-    if (j < t.nk[0]) {
-      src = 0;
-      return t.k[0].start + j;
-    }
-    j -= t.nk[0];
-    src = 1;
-    if (j < t.nk[1]) return t.k[1].start + j;
-    return t.k[2].start + (j - t.nk[1]);
+// Key blocks never straddle two key runs: every run starts on a 64-key block
+// boundary (the padding keys are masked), so which buffer a block comes from
+// is a per-block scalar.  Block kb covers keys [off, off + 64) of run `run`, of
+// which `valid` (possibly more than 64) exist.
+struct BlockInfo {
+  int run, off, valid;
+};
+
+__device__ __forceinline__ int pad_blocks(int n) { return (n + kBN - 1) / kBN; }
+
+__device__ __forceinline__ BlockInfo block_info(const TileRuns& t, int kb) {
+  const int b0 = pad_blocks(t.nk[0]), b1 = pad_blocks(t.nk[1]);
+  BlockInfo bi;
+  if (kb < b0) {
+    bi.run = 0;
+    bi.off = kb * kBN;
+  } else if (kb < b0 + b1) {
+    bi.run = 1;
+    bi.off = (kb - b0) * kBN;
   } else {
-    src = 0;
-    const int r = fast_div(j, t.k[0].row_len, inv_len);
-    return t.k[0].start + r * t.k[0].pitch + (j - r * t.k[0].row_len);
+    bi.run = 2;
+    bi.off = (kb - b0 - b1) * kBN;
   }
+  // selects, not a dynamic index: indexing the run arrays at run time would
+  // move the whole struct to scratch memory
+  const int nk = bi.run == 0 ? t.nk[0] : (bi.run == 1 ? t.nk[1] : t.nk[2]);
+  bi.valid = nk - bi.off;
+  return bi;
+}
+
+// field by field: a select between two struct lvalues selects their addresses
+__device__ __forceinline__ Run block_run(const TileRuns& t, int run) {
+  auto pick = [run](int a, int b, int c) { return run == 0 ? a : (run == 1 ? b : c); };
+  return Run{pick(t.k[0].start, t.k[1].start, t.k[2].start), pick(t.k[0].row_len, t.k[1].row_len, t.k[2].row_len),
+             pick(t.k[0].rows, t.k[1].rows, t.k[2].rows), pick(t.k[0].pitch, t.k[1].pitch, t.k[2].pitch)};
+}
+
+// Token of key j of run r (strips: runs are contiguous; windows: one run of rows).
+template <int MODE>
+__device__ __forceinline__ int run_token(const Run& r, int j, float inv_len) {
+  if (MODE == NPA_MODE_STRIPS) return r.start + j;
+  const int row = fast_div(j, r.row_len, inv_len);
+  return r.start + row * r.pitch + (j - row * r.row_len);
 }
 
 // exp2 of 16 accumulator entries, packed to bf16 pairs for the PV operand;
@@ -223,10 +250,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   const uint32_t sn2 = (uint32_t)a.sn * 2u;  // token stride in bytes
 
   const rsrc_t rq = make_rsrc((const __bf16*)a.q + bh, a.range_bytes);
-  const rsrc_t rkf = make_rsrc((const __bf16*)a.kf + bh, a.range_bytes);
-  const rsrc_t rvf = make_rsrc((const __bf16*)a.vf + bh, a.range_bytes);
-  const rsrc_t rks = make_rsrc((const __bf16*)a.ks + bh, a.range_bytes);
-  const rsrc_t rvs = make_rsrc((const __bf16*)a.vs + bh, a.range_bytes);
+  const __bf16* kf_base = (const __bf16*)a.kf + bh;
+  const __bf16* vf_base = (const __bf16*)a.vf + bh;
+  const __bf16* ks_base = (const __bf16*)a.ks + bh;
+  const __bf16* vs_base = (const __bf16*)a.vs + bh;
   const rsrc_t ro = make_rsrc((__bf16*)a.o + bh, a.range_bytes);
 
   // ---- Q^T fragments, pre-multiplied by scale*log2(e):
@@ -264,29 +291,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   // row-major with the 16-byte chunks of row r XOR-permuted by swz(r); keys past
   // the end of the set read zeros (out-of-range offset).
   auto fetch = [&](int kb, __bf16* skd, __bf16* svd) {
+    const BlockInfo bi = block_info(tr, kb);
+    const Run run = block_run(tr, bi.run);
+    // runs 1 and 2 are the stale halos; the descriptor is built from the chosen
+    // base pointer (a select between two descriptors would be lowered through memory)
+    const bool stale = MODE == NPA_MODE_STRIPS && bi.run != 0;
+    const rsrc_t rk = make_rsrc(stale ? ks_base : kf_base, a.range_bytes);
+    const rsrc_t rv = make_rsrc(stale ? vs_base : vf_base, a.range_bytes);
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
       const int inst = wave * CH + r;
       const int pos = inst * 64 + lane;  // chunk slot in the tile
       const int row = pos / CPR, slot = pos % CPR;
-      const int kidx = kb * kBN + row;
-      int src = 0;
       uint32_t off = kOOB;
-      if (kidx < nk) off = (uint32_t)key_token<MODE>(tr, kidx, inv_klen, src) * sn2 + (slot ^ swz(row)) * 16;
+      if (row < bi.valid)
+        off = (uint32_t)run_token<MODE>(run, bi.off + row, inv_klen) * sn2 + (slot ^ swz(row)) * 16;
       lds_ptr dk = (lds_ptr)&skd[inst * 512];
       lds_ptr dv = (lds_ptr)&svd[inst * 512];
-      if (MODE == NPA_MODE_STRIPS && src) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, dk, 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, dv, 16, off, 0, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkf, dk, 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvf, dv, 16, off, 0, 0, 0);
-      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk, 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dv, 16, off, 0, 0, 0);
     }
   };
 
   f32x16 o[DT][NT];
-  float nm[NT];  // -m: broadcast into the C operand of the first S^T MFMA
+  f32x16 shift[NT];  // -m in every entry: C operand of the first S^T MFMA
   float l[NT];
 
   // row of the K tile this lane feeds into the S^T product: bits 2,3 of l32 swapped
@@ -294,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   // ds_read_b64_tr_b16 source address pattern for the V^T fragments
   const int vkey = 8 * g + ((lane & 15) >> 2);
   const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int nkb = (nk + kBN - 1) / kBN;
+  const int nkb = pad_blocks(tr.nk[0]) + pad_blocks(tr.nk[1]) + pad_blocks(tr.nk[2]);
 
   // Exact row max of the whole tile (the rare second pass only): S^T with a
   // zero shift, reduced over every key.
@@ -315,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? f32x16{} : s[nt]);
         }
-        const int base = nk - kb * kBN - mt * 32;
+        const int base = block_info(tr, kb).valid - mt * 32;
         const int t = base - 8 * g;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -361,16 +389,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
           const int row = mt * 32 + krow;
           const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f32x16 c0;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) c0[j] = nm[nt];
-            s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? c0 : s[nt]);
-          }
+          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : s[nt]);
         }
         // ---- keys past the end of the tile's set (last block only):
         // entry j of lane half g is key 8g + j (j < 8) or 8g + j + 8 (j >= 8)
-        const int base = nk - kb * kBN - mt * 32;
+        const int base = block_info(tr, kb).valid - mt * 32;
         if (base < 32) {
           const int t = base - 8 * g;
 #pragma unroll
@@ -388,7 +411,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
           for (int nt = 0; nt < NT; ++nt) {
             const float m = pair_max(max16(s[nt]));
             l[nt] = exp_pack(s[nt], m, p0[nt], p1[nt]);
-            nm[nt] = -m;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) shift[nt][j] = -m;
           }
         } else {
 #pragma unroll
@@ -426,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   __shared__ int redo;
   if (tid == 0) redo = 0;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) nm[nt] = 0.0f;
+  for (int nt = 0; nt < NT; ++nt) shift[nt] = f32x16{};
   pass(false);
   bool bad = false;
 #pragma unroll
@@ -437,7 +461,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
     float mx[NT];
     row_max(mx);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) nm[nt] = -mx[nt];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) shift[nt][j] = -mx[nt];
     pass(true);
   }
 
