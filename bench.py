@@ -74,6 +74,9 @@ def main() -> int:
     ap.add_argument("--workload", default="sdxl4096_npa")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (outside the timed region) so that a "
+                         "counter profile of this command can scale its byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the partial-attention path is built and timed on a single MI355X; "
@@ -116,6 +119,13 @@ def main() -> int:
             ev[1].record()
         npa.sg_blend(x, ref, sgw["w_t"], sgw["sigma"], out=sg_out)
 
+    if args.copy_calibration:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 512 MiB read + 512 MiB written")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -95,6 +95,15 @@ int64_t pairs_per_bh(const npa::Geo& g) {
   return total;
 }
 
+// Does any tile have a key run that is not a whole number of 64-key blocks?
+bool has_partial_blocks(const npa::Geo& g) {
+  for (int32_t t = 0; t < g.n_tiles; ++t) {
+    const npa::TileRuns r = npa::tile_runs(g, t);
+    if (r.nk[0] % 64 || r.nk[1] % 64 || r.nk[2] % 64) return true;
+  }
+  return false;
+}
+
 bool reads_stale(const npa::Geo& g) {
   for (int32_t t = 0; t < g.n_tiles; ++t) {
     const npa::TileRuns r = npa::tile_runs(g, t);
@@ -204,6 +213,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
                 (long long)range);
   npa::AttnArgs a;
   a.range_bytes = (uint32_t)(range > 0xFFFFFFFFll ? 0xFFFFFFFFll : range);
+  a.partial = has_partial_blocks(g) ? 1 : 0;
   a.q = Q;
   a.kf = K_fresh;
   a.vf = V_fresh;

@@ -38,6 +38,8 @@
 // queries read zeros / drop their stores without branches.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "npa_internal.hpp"
 
 namespace npa {
@@ -61,15 +63,29 @@ constexpr int kBN = 64;                  // keys per LDS block
 constexpr uint32_t kOOB = 0x7FFFFFF0u;   // byte offset past every buffer's range
 constexpr float kOverflow = 1.152921504606846976e18f;  // 2^60
 
+#ifndef NPA_NT64
+#define NPA_NT64 2
+#endif
+#ifndef NPA_NT128
+#define NPA_NT128 1
+#endif
+#ifndef NPA_MINB64
+#define NPA_MINB64 2
+#endif
+#ifndef NPA_MINB128
+#define NPA_MINB128 2
+#endif
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<64> {
-  static constexpr int NT = 2;  // 64 queries per wave
+  static constexpr int NT = NPA_NT64;  // 32*NT queries per wave
+  static constexpr int MINB = NPA_MINB64;  // workgroups per CU the register budget is sized for
 };
 template <>
 struct Cfg<128> {
-  static constexpr int NT = 1;  // 32 queries per wave
+  static constexpr int NT = NPA_NT128;
+  static constexpr int MINB = NPA_MINB128;
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD runs one
@@ -210,8 +226,10 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return m;
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
+// PARTIAL: some key run of the plan is not a multiple of 64 keys, so some
+// blocks end inside the padding and need masking (instantiated only then).
+template <int D, int MODE, bool PARTIAL>
+__global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int NT = Cfg<D>::NT;
   constexpr int ROWS = 32 * NT;
   constexpr int BM = kWaves * ROWS;
@@ -290,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   // picks the global chunk that belongs at its slot, so the tile is stored
   // row-major with the 16-byte chunks of row r XOR-permuted by swz(r); keys past
   // the end of the set read zeros (out-of-range offset).
-  auto fetch = [&](int kb, __bf16* skd, __bf16* svd) {
+  auto fetch = [&](int kb, __bf16* skd, __bf16* svd) __attribute__((always_inline)) {
     const BlockInfo bi = block_info(tr, kb);
     const Run run = block_run(tr, bi.run);
     // runs 1 and 2 are the stale halos; the descriptor is built from the chosen
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
 
   // Exact row max of the whole tile (the rare second pass only): S^T with a
   // zero shift, reduced over every key.
-  auto row_max = [&](float (&mx)[NT]) {
+  auto row_max = [&](float (&mx)[NT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
     auto block = [&](int kb, const __bf16* skb, __bf16* skn, __bf16* svn) {
@@ -367,79 +385,166 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   // no rescale inside the loop.  preset=false: the shift is the exact row max
   // of the first 32 keys.  preset=true: the shift was set beforehand (the true
   // row max of the tile).
-  auto pass = [&](bool preset) {
+  //
+  // Each 64-key block is one straight-line body, specialised at compile time
+  // for the first block (FIRST: scores unshifted, the max is taken) and for
+  // blocks that end inside the padding (MASK): the score MFMAs of both 32-key
+  // halves are issued before the first half's exp work, so the second half's
+  // MFMAs run while the VALU does the first half's softmax.
+  auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn, auto first_tag,
+                   auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // this wave's copies into tile kb are done; after the barrier, everyone's are
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
+    const int valid = MASK ? block_info(tr, kb).valid : kBN;
+
+    // S^T of half mt (exp2 domain; shifted by -m unless FIRST)
+    auto scores = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int row = mt * 32 + krow;
+        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          sc[nt] = mfma(kf, qf[nt][ks], ks == 0 ? (FIRST ? f32x16{} : shift[nt]) : sc[nt]);
+      }
+    };
+    // keys past the end of their run: entry j of lane half g is key 8g + j
+    // (j < 8) or 8g + j + 8 (j >= 8) of the half
+    auto mask = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
+      if (!MASK) return;
+      const int t = valid - mt * 32 - 8 * g;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((j < 8 ? j : j + 8) >= t)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sc[nt][j] = -INFINITY;
+    };
+    // O^T += V^T P^T over half mt
+    auto pv = [&](int mt, const bf16x8 (&p0)[NT], const bf16x8 (&p1)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int r0 = mt * 32 + 16 * h2 + vkey, r1 = r0 + 4;
+          const int col = 32 * dt + vdim;  // multiple of 4: one 8-byte half of a chunk
+          const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
+          const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
+          const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma(vf, h2 ? p1[nt] : p0[nt], o[dt][nt]);
+        }
+      }
+    };
+
+    // Instruction counts of the phases, for the interleave patterns below.
+    constexpr int kSMfma = KS * NT;        // MFMAs of one half's S^T
+    constexpr int kSReads = KS;            // its K-fragment reads
+    constexpr int kPVMfma = DT * 2 * NT;   // MFMAs of one half's PV
+    constexpr int kPVReads = DT * 4;       // its V^T transpose reads
+    constexpr int kExpValu = NT * 33;      // exp, pack, row-sum VALU of one half
+
+    f32x16 s0[NT], s1[NT];
+    bf16x8 pa0[NT], pa1[NT], pb0[NT], pb1[NT];
+    if (MASK && !FIRST) {
+      // a block that ends inside the padding (at most one per key run): the
+      // halves one after the other, which keeps only one score tile live
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        __builtin_amdgcn_sched_barrier(0);
+        scores(mt, s0);
+        mask(mt, s0);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s0[nt], pa0[nt], pa1[nt]);
+        pv(mt, pa0, pa1);
+      }
+      return;
+    }
+    scores(0, s0);
+    mask(0, s0);
+    if (FIRST) {
+      // the exact row max of the first 32 keys becomes the shift; half 1 then
+      // takes the ordinary path with the shift inside its MFMA
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float m = pair_max(max16(s0[nt]));
+        l[nt] += exp_pack(s0[nt], m, pa0[nt], pa1[nt]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) shift[nt][j] = -m;
+      }
+      pv(0, pa0, pa1);
+      __builtin_amdgcn_sched_barrier(0);
+      // (scores() reads FIRST, so half 1 is written out with the shift here)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int row = 32 + krow;
+        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s1[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : s1[nt]);
+      }
+      mask(1, s1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s1[nt], pb0[nt], pb1[nt]);
+      pv(1, pb0, pb1);
+      return;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // half 1's score MFMAs run while the VALU turns half 0's scores into weights
+    scores(1, s1);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s0[nt], pa0[nt], pa1[nt]);
+#pragma unroll
+    for (int i = 0; i < kSMfma; ++i) {
+      if (i < kSReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);   // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mask(1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    // half 0's PV MFMAs run while the VALU does half 1's weights
+    pv(0, pa0, pa1);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s1[nt], pb0[nt], pb1[nt]);
+#pragma unroll
+    for (int i = 0; i < kPVMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kPVReads / kPVMfma, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kPVMfma, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(1, pb0, pb1);
+  };
+  // block kb of the pass, picking the body for partial blocks at run time
+  auto any_block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn) __attribute__((always_inline)) {
+    if (PARTIAL && block_info(tr, kb).valid < kBN)
+      block(kb, skb, svb, skn, svn, std::false_type{}, std::integral_constant<bool, PARTIAL>{});
+    else
+      block(kb, skb, svb, skn, svn, std::false_type{}, std::false_type{});
+  };
+  auto pass = [&](bool preset) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x16{};
       l[nt] = 0.0f;
     }
-    auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn) {
-      // this wave's copies into tile kb are done; after the barrier, everyone's are
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        // ---- S^T (already in the exp2 domain, already shifted by -m)
-        f32x16 s[NT];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int row = mt * 32 + krow;
-          const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : s[nt]);
-        }
-        // ---- keys past the end of the tile's set (last block only):
-        // entry j of lane half g is key 8g + j (j < 8) or 8g + j + 8 (j >= 8)
-        const int base = block_info(tr, kb).valid - mt * 32;
-        if (base < 32) {
-          const int t = base - 8 * g;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if ((j < 8 ? j : j + 8) >= t)
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) s[nt][j] = -INFINITY;
-          }
-        }
-        // ---- weights
-        bf16x8 p0[NT], p1[NT];
-        if (kb == 0 && mt == 0 && !preset) {
-          // first sub-block: its exact row max becomes the shift
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float m = pair_max(max16(s[nt]));
-            l[nt] = exp_pack(s[nt], m, p0[nt], p1[nt]);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) shift[nt][j] = -m;
-          }
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s[nt], p0[nt], p1[nt]);
-        }
-        // ---- O^T += V^T P^T over the sub-block's 32 keys
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int r0 = mt * 32 + 16 * h2 + vkey, r1 = r0 + 4;
-            const int col = 32 * dt + vdim;  // multiple of 4: one 8-byte half of a chunk
-            const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
-            const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
-            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
-            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
-            const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma(vf, h2 ? p1[nt] : p0[nt], o[dt][nt]);
-          }
-        }
-      }
-    };
     fetch(0, sk0, sv0);
-    for (int kb = 0; kb < nkb; kb += 2) {
-      block(kb, sk0, sv0, sk1, sv1);
-      if (kb + 1 < nkb) block(kb + 1, sk1, sv1, sk0, sv0);
+    if (preset)
+      any_block(0, sk0, sv0, sk1, sv1);
+    else if (PARTIAL && block_info(tr, 0).valid < kBN)
+      block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::integral_constant<bool, PARTIAL>{});
+    else
+      block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::false_type{});
+    for (int kb = 1; kb < nkb; kb += 2) {
+      any_block(kb, sk1, sv1, sk0, sv0);
+      if (kb + 1 < nkb) any_block(kb + 1, sk0, sv0, sk1, sv1);
     }
   };
 
@@ -448,23 +553,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(const AttnArgs a
   // Then the workgroup computes every row's true max and runs the pass again
   // with that shift, where every weight is <= 1 and the max itself weighs 1.
   __shared__ int redo;
-  if (tid == 0) redo = 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) shift[nt] = f32x16{};
-  pass(false);
-  bool bad = false;
+  // At most two passes, one copy of the pass code: the second pass runs only
+  // when the first one's row sums left [1, 2^60].
+  bool preset = false;
+  for (;;) {
+    if (tid == 0) redo = 0;
+    pass(preset);
+    if (preset) break;
+    bool bad = false;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bad |= !(pair_sum(l[nt]) <= kOverflow);
-  if (wave_any(bad) && lane == 0) redo = 1;  // every writer stores 1
-  __syncthreads();
-  if (redo) {
+    for (int nt = 0; nt < NT; ++nt) bad |= !(pair_sum(l[nt]) <= kOverflow);
+    __syncthreads();
+    if (wave_any(bad) && lane == 0) redo = 1;  // every writer stores 1
+    __syncthreads();
+    if (!redo) break;
     float mx[NT];
     row_max(mx);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) shift[nt][j] = -mx[nt];
-    pass(true);
+    preset = true;
   }
 
   // ---- normalise and store: lane (query, g) holds dims 32dt + 8*j4 + 4g .. +4
@@ -493,18 +604,26 @@ int attn_bf16_block_m(int head_dim) {
   return 0;
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int /*block_m*/, hipStream_t st) {
+template <int D, int MODE>
+void launch_dm(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.nblocks), block(kThreads);
+  if (a.partial)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, false>), grid, block, 0, st, a);
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int /*block_m*/, hipStream_t st) {
   if (head_dim == 64) {
     if (a.g.mode == NPA_MODE_STRIPS)
-      hipLaunchKernelGGL((attn_bf16_kernel<64, NPA_MODE_STRIPS>), grid, block, 0, st, a);
+      launch_dm<64, NPA_MODE_STRIPS>(a, st);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, NPA_MODE_WINDOW>), grid, block, 0, st, a);
+      launch_dm<64, NPA_MODE_WINDOW>(a, st);
   } else {
     if (a.g.mode == NPA_MODE_STRIPS)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, NPA_MODE_STRIPS>), grid, block, 0, st, a);
+      launch_dm<128, NPA_MODE_STRIPS>(a, st);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<128, NPA_MODE_WINDOW>), grid, block, 0, st, a);
+      launch_dm<128, NPA_MODE_WINDOW>(a, st);
   }
   return hipGetLastError();
 }

@@ -92,6 +92,7 @@ struct AttnArgs {
   float scale;      // softmax scale
   float c;          // scale * log2(e)
   uint32_t range_bytes;  // bytes spanned by one (batch, head) slice: ((N-1)*sn + d) * esize
+  int32_t partial;       // some key run is not a multiple of 64 keys
 };
 
 // Arguments of the structure-guidance kernel.
