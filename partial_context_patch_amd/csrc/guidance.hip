@@ -7,7 +7,9 @@
 // produces a 32x64 output tile: the tile plus an R-pixel apron of (ref - x)
 // is staged in LDS, filtered along rows into a second LDS buffer, then along
 // columns straight into the output.  Bandwidth-bound: x and ref are read once
-// from HBM (the apron re-reads hit L2), out is written once.
+// from HBM (the apron re-reads hit L2), out is written once: 12 bytes of HBM
+// traffic per element.  sg_blend_fixed is the radius-12 (sigma = 4) form;
+// sg_blend_kernel serves any other radius.
 //
 // asg_blend: out = eps + w * mask * (eps_ref_prev - eps), element-wise
 // (asynchronous structure guidance, pith.science verdict on ASGDiffusion,
@@ -67,6 +69,118 @@ __global__ __launch_bounds__(kThreads) void sg_blend_kernel(const SgArgs a) {
   }
 }
 
+
+// Radius known at compile time (sigma = 4 -> R = 12): 64 x 32 output tile,
+// every thread produces 8 outputs per pass from a register window of 8 + 2R
+// inputs, so each staged value is read from LDS about (8 + 2R) / 8 times
+// instead of 2R + 1 times, and no index needs a run-time division.
+template <int R>
+__global__ __launch_bounds__(kThreads) void sg_blend_fixed(const SgArgs a) {
+  constexpr int LW = kTW + 2 * R, LH = kTH + 2 * R, WIN = 8 + 2 * R;
+  __shared__ __attribute__((aligned(16))) float diff[LH * LW];
+  __shared__ float tmp[LH * kTW];
+  __shared__ __attribute__((aligned(16))) float xs[kTH * kTW];  // x over the output tile itself
+  const int r0 = blockIdx.y * kTH, c0 = blockIdx.x * kTW;
+  const size_t pb = (size_t)blockIdx.z * a.H * a.W;
+  const float* x = a.x + pb;
+  const float* ref = a.ref + pb;
+  float taps[2 * R + 1];
+#pragma unroll
+  for (int t = 0; t <= 2 * R; ++t) taps[t] = a.taps[t];
+
+  // stage ref - x over the tile and its apron.  Tiles whose apron lies inside
+  // the image read 16-byte vectors; the others reflect (101) index by index.
+  // Fixed, unrolled trip counts let every load of a thread be in flight at once.
+  static_assert(LW % 4 == 0 && R % 4 == 0 && kTW % 4 == 0, "vector staging");
+  const bool inside = r0 - R >= 0 && c0 - R >= 0 && r0 + kTH + R <= a.H && c0 + kTW + R <= a.W && (a.W & 3) == 0;
+  if (inside) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int LW4 = LW / 4;
+    constexpr int kStage4 = (LH * LW4 + kThreads - 1) / kThreads;
+    f32x4 rv[kStage4], xv[kStage4];
+#pragma unroll
+    for (int k = 0; k < kStage4; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      const int rr = i / LW4, c4 = i - rr * LW4;
+      const size_t at = (size_t)(r0 - R + rr) * a.W + (c0 - R + 4 * c4);
+      rv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      xv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < LH * LW4) {
+        rv[k] = *(const f32x4*)(ref + at);
+        xv[k] = *(const f32x4*)(x + at);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kStage4; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < LH * LW4) {
+        *(f32x4*)&diff[4 * i] = rv[k] - xv[k];
+        const int rr = i / LW4 - R, cc = 4 * (i % LW4) - R;
+        if (rr >= 0 && rr < kTH && cc >= 0 && cc < kTW) *(f32x4*)&xs[rr * kTW + cc] = xv[k];
+      }
+    }
+  } else {
+  constexpr int kStage = (LH * LW + kThreads - 1) / kThreads;
+  float rv[kStage], xv[kStage];
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    const int rr = i / LW, cc = i - rr * LW;
+    int gr = r0 - R + rr, gc = c0 - R + cc;
+    if ((unsigned)gr >= (unsigned)a.H) gr = reflect101(gr, a.H);
+    if ((unsigned)gc >= (unsigned)a.W) gc = reflect101(gc, a.W);
+    const size_t at = (size_t)gr * a.W + gc;
+    rv[k] = 0.0f;
+    xv[k] = 0.0f;
+    if (i < LH * LW) {
+      rv[k] = ref[at];
+      xv[k] = x[at];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < LH * LW) {
+      diff[i] = rv[k] - xv[k];
+      const int rr = i / LW - R, cc = i % LW - R;
+      if (rr >= 0 && rr < kTH && cc >= 0 && cc < kTW) xs[rr * kTW + cc] = xv[k];
+    }
+  }
+  }
+  __syncthreads();
+  // rows: thread -> (row, 8-column segment); LH rows x 8 segments
+  for (int job = threadIdx.x; job < LH * (kTW / 8); job += kThreads) {
+    const int rr = job >> 3, cs = (job & 7) * 8;
+    float w[WIN];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) w[k] = diff[rr * LW + cs + k];
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(taps[t], w[o + t], acc);
+      tmp[rr * kTW + cs + o] = acc;
+    }
+  }
+  __syncthreads();
+  // columns: thread -> (column, 8-row segment); 64 columns x 4 segments
+  {
+    const int cc = threadIdx.x & (kTW - 1), rs = (threadIdx.x >> 6) * 8;
+    float w[WIN];
+#pragma unroll
+    for (int k = 0; k < WIN; ++k) w[k] = tmp[(rs + k) * kTW + cc];
+    const int gc = c0 + cc;
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+      const int gr = r0 + rs + o;
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(taps[t], w[o + t], acc);
+      if (gr < a.H && gc < a.W) a.out[pb + (size_t)gr * a.W + gc] = __builtin_fmaf(a.w, acc, xs[(rs + o) * kTW + cc]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* __restrict__ eps,
                                                              const float* __restrict__ ref,
                                                              const float* __restrict__ mask,
@@ -94,6 +208,11 @@ __global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* __rest
 
 hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st) {
   const dim3 grid((a.W + kTW - 1) / kTW, (a.H + kTH - 1) / kTH, a.planes), block(kThreads);
+  static_assert(kTH == 32 && kTW == 64 && kThreads == 256, "sg_blend_fixed thread mapping");
+  if (a.R == 12) {
+    hipLaunchKernelGGL((sg_blend_fixed<12>), grid, block, 0, st, a);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(float) * ((size_t)(kTH + 2 * a.R) * (kTW + 2 * a.R) + (size_t)(kTH + 2 * a.R) * kTW);
   hipLaunchKernelGGL(sg_blend_kernel, grid, block, lds, st, a);
   return hipGetLastError();
