@@ -34,7 +34,8 @@ def log(msg: str) -> None:
 
 
 def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
-    """The oracle (as it is) on whole query tiles of (batch 0, head 0) until the budget is spent."""
+    """The oracle (as it is) on whole query tiles, (batch, head) pair after pair,
+    until the time budget is spent; the rate is its useful flops per second."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -47,11 +48,15 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
     H, W, d = w["map_h"], w["map_w"], w["head_dim"]
     tiles = list(A.iter_tiles(H, W, spec))
     done_pairs, n_tiles, t0 = 0, 0, time.perf_counter()
-    for qt, ft, st in tiles:
-        A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec,
-                          query_tokens=qt, heads=[(0, 0)])
-        done_pairs += len(qt) * (len(ft) + len(st))
-        n_tiles += 1
+    heads = [(b, j) for b in range(w["batch"]) for j in range(w["heads"])]
+    for b, j in heads:
+        for qt, ft, st in tiles:
+            A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec,
+                              query_tokens=qt, heads=[(b, j)])
+            done_pairs += len(qt) * (len(ft) + len(st))
+            n_tiles += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
         if time.perf_counter() - t0 >= budget_s:
             break
     secs = time.perf_counter() - t0
@@ -61,8 +66,9 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n_tiles} of {len(tiles)} query tiles of batch 0, head 0 ({done_pairs} attended pairs) "
-                  f"in {secs:.1f} s; fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}",
+        "sample": f"{n_tiles} (batch, head, query tile) units of {len(tiles) * len(heads)} "
+                  f"({done_pairs} attended pairs, {4 * d * done_pairs / 1e9:.1f} useful GFLOP) in {secs:.1f} s; "
+                  f"fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}",
     }
 
 
@@ -72,7 +78,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sdxl4096_npa")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (outside the timed region) so that a "
@@ -118,6 +124,8 @@ def main() -> int:
         if ev is not None:
             ev[1].record()
         npa.sg_blend(x, ref, sgw["w_t"], sgw["sigma"], out=sg_out)
+        if ev is not None:
+            ev[2].record()
 
     if args.copy_calibration:
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
@@ -129,7 +137,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -140,12 +148,18 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(stop) / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sg_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_avg = float(np.mean(attn_ms))
+    sg_avg = float(np.mean(sg_ms))
     log(f"step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms); attention avg {attn_avg:.4f} ms "
         f"median {float(np.median(attn_ms)):.4f} min {min(attn_ms):.4f} max {max(attn_ms):.4f}")
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_avg * 1e-3) / 1e12
+    # structure-guidance blend: reads x and ref, writes out, 4 bytes each per element
+    sg_bytes = 12 * sgw["channels"] * sgw["map_h"] * sgw["map_w"]
+    from partial_context_patch_amd import profiling
+    traffic = profiling.load_traffic(name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -175,8 +189,12 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) activations of the workload's shape; no weights or datasets)",
         "config": cfg,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else int(traffic),
                      "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg, 5)},
+        "sg_blend": {"bound": "hbm", "achieved": round(sg_bytes / (sg_avg * 1e-3) / 1e9, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(sg_bytes / (sg_avg * 1e-3) / 1e9 / 8000.0, 4),
+                     "algorithmic_bytes": sg_bytes, "avg_launch_ms": round(sg_avg, 5)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
