@@ -8,10 +8,10 @@
 // score matrix never leaves registers and K/V are read in place from the
 // fresh and stale buffers (never concatenated).
 //
-// Workgroup = 4 waves; each wave owns ROWS = 32*NT queries of one tile.  The
-// workgroup walks the tile's keys in blocks of 64 staged through a
-// double-buffered LDS tile (one barrier per block); each wave consumes a block
-// as two 32-key sub-blocks.
+// Workgroup = WAVES waves (4 at d = 64, 8 at d = 128); each wave owns
+// ROWS = 32*NT queries of one tile.  The workgroup walks the tile's keys in
+// blocks of 64 staged through a double-buffered LDS tile (one barrier per
+// block); each wave consumes a block as two 32-key sub-blocks.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, lane l: column l%32, half g=l/32):
 //   S^T = K * Q^T   A = K rows (keys),  B = Q^T (queries in columns)
@@ -57,35 +57,40 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;                  // keys per LDS block
 constexpr uint32_t kOOB = 0x7FFFFFF0u;   // byte offset past every buffer's range
 constexpr float kOverflow = 1.152921504606846976e18f;  // 2^60
 
+// Per head size: NT = 32-query column tiles per wave, WAVES = waves per
+// workgroup (all sharing the workgroup's K/V tiles), MINB = workgroups per CU
+// the register budget is sized for (two waves per SIMD either way).  d = 128
+// takes eight waves: its K/V tiles are twice as large per query, and sharing
+// them among more queries halves the copies per MFMA.
 #ifndef NPA_NT64
 #define NPA_NT64 2
+#endif
+#ifndef NPA_WAVES64
+#define NPA_WAVES64 4
 #endif
 #ifndef NPA_NT128
 #define NPA_NT128 1
 #endif
-#ifndef NPA_MINB64
-#define NPA_MINB64 2
-#endif
-#ifndef NPA_MINB128
-#define NPA_MINB128 2
+#ifndef NPA_WAVES128
+#define NPA_WAVES128 8
 #endif
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<64> {
-  static constexpr int NT = NPA_NT64;  // 32*NT queries per wave
-  static constexpr int MINB = NPA_MINB64;  // workgroups per CU the register budget is sized for
+  static constexpr int NT = NPA_NT64;
+  static constexpr int WAVES = NPA_WAVES64;
+  static constexpr int MINB = 8 / WAVES;
 };
 template <>
 struct Cfg<128> {
   static constexpr int NT = NPA_NT128;
-  static constexpr int MINB = NPA_MINB128;
+  static constexpr int WAVES = NPA_WAVES128;
+  static constexpr int MINB = 8 / WAVES;
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD runs one
@@ -135,40 +140,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // Key blocks never straddle two key runs: every run starts on a 64-key block
 // boundary (the padding keys are masked), so which buffer a block comes from
-// is a per-block scalar.  Block kb covers keys [off, off + 64) of run `run`, of
-// which `valid` (possibly more than 64) exist.
-struct BlockInfo {
-  int run, off, valid;
-};
-
+// is a per-block scalar.
 __device__ __forceinline__ int pad_blocks(int n) { return (n + kBN - 1) / kBN; }
-
-__device__ __forceinline__ BlockInfo block_info(const TileRuns& t, int kb) {
-  const int b0 = pad_blocks(t.nk[0]), b1 = pad_blocks(t.nk[1]);
-  BlockInfo bi;
-  if (kb < b0) {
-    bi.run = 0;
-    bi.off = kb * kBN;
-  } else if (kb < b0 + b1) {
-    bi.run = 1;
-    bi.off = (kb - b0) * kBN;
-  } else {
-    bi.run = 2;
-    bi.off = (kb - b0 - b1) * kBN;
-  }
-  // selects, not a dynamic index: indexing the run arrays at run time would
-  // move the whole struct to scratch memory
-  const int nk = bi.run == 0 ? t.nk[0] : (bi.run == 1 ? t.nk[1] : t.nk[2]);
-  bi.valid = nk - bi.off;
-  return bi;
-}
-
-// field by field: a select between two struct lvalues selects their addresses
-__device__ __forceinline__ Run block_run(const TileRuns& t, int run) {
-  auto pick = [run](int a, int b, int c) { return run == 0 ? a : (run == 1 ? b : c); };
-  return Run{pick(t.k[0].start, t.k[1].start, t.k[2].start), pick(t.k[0].row_len, t.k[1].row_len, t.k[2].row_len),
-             pick(t.k[0].rows, t.k[1].rows, t.k[2].rows), pick(t.k[0].pitch, t.k[1].pitch, t.k[2].pitch)};
-}
 
 // Token of key j of run r (strips: runs are contiguous; windows: one run of rows).
 template <int MODE>
@@ -179,8 +152,8 @@ __device__ __forceinline__ int run_token(const Run& r, int j, float inv_len) {
 }
 
 // exp2 of 16 accumulator entries, packed to bf16 pairs for the PV operand;
-// returns the sum of the packed (bf16) weights.
-__device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8& p0, bf16x8& p1) {
+// returns s plus the sum of the packed (bf16) weights.
+__device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8& p0, bf16x8& p1, float s) {
   f32x8 a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -190,7 +163,6 @@ __device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8
   p0 = __builtin_convertvector(a, bf16x8);
   p1 = __builtin_convertvector(b, bf16x8);
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
@@ -200,7 +172,7 @@ __device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8
 }
 
 // Same without a shift argument (the common path: the shift is inside acc).
-__device__ __forceinline__ float exp_pack0(const f32x16& acc, bf16x8& p0, bf16x8& p1) {
+__device__ __forceinline__ float exp_pack0(const f32x16& acc, bf16x8& p0, bf16x8& p1, float s) {
   f32x8 a, b;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -210,7 +182,6 @@ __device__ __forceinline__ float exp_pack0(const f32x16& acc, bf16x8& p0, bf16x8
   p0 = __builtin_convertvector(a, bf16x8);
   p1 = __builtin_convertvector(b, bf16x8);
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
@@ -229,7 +200,9 @@ __device__ __forceinline__ float max16(const f32x16& a) {
 // PARTIAL: some key run of the plan is not a multiple of 64 keys, so some
 // blocks end inside the padding and need masking (instantiated only then).
 template <int D, int MODE, bool PARTIAL>
-__global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_kernel(const AttnArgs a) {
+  constexpr int kWaves = Cfg<D>::WAVES;
+  constexpr int kThreads = 64 * kWaves;
   constexpr int NT = Cfg<D>::NT;
   constexpr int ROWS = 32 * NT;
   constexpr int BM = kWaves * ROWS;
@@ -248,7 +221,9 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
   __shared__ __attribute__((aligned(16))) __bf16 sv0[kBN * LDR];
   __shared__ __attribute__((aligned(16))) __bf16 sv1[kBN * LDR];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index as a uniform value: everything derived from it (LDS tile slots,
+  // the DMA destinations) stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
   const int bid = xcd_remap(blockIdx.x, a.nblocks);
@@ -308,27 +283,92 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
   // picks the global chunk that belongs at its slot, so the tile is stored
   // row-major with the 16-byte chunks of row r XOR-permuted by swz(r); keys past
   // the end of the set read zeros (out-of-range offset).
-  auto fetch = [&](int kb, __bf16* skd, __bf16* svd) __attribute__((always_inline)) {
-    const BlockInfo bi = block_info(tr, kb);
-    const Run run = block_run(tr, bi.run);
-    // runs 1 and 2 are the stale halos; the descriptor is built from the chosen
-    // base pointer (a select between two descriptors would be lowered through memory)
-    const bool stale = MODE == NPA_MODE_STRIPS && bi.run != 0;
-    const rsrc_t rk = make_rsrc(stale ? ks_base : kf_base, a.range_bytes);
-    const rsrc_t rv = make_rsrc(stale ? vs_base : vf_base, a.range_bytes);
+  //
+  // The slot a lane fills is the same in every block: key row krow_c[r] of the
+  // block, at byte lane_off[r] from the block's first key when the block's keys
+  // are consecutive tokens.  Per block only uniform values change, and they are
+  // kept in a cursor that advances one block per fetch (blocks are always
+  // fetched in order 0, 1, ..., nkb-1): the key run, the keys of the run left
+  // from the block's first key (the block's valid count when below 64), that
+  // key's byte offset and, in a window, its column; keys of the block at or
+  // past lim1 (lim2) lie one (two) window rows further down.
+  int krow_c[CH];
+  uint32_t lane_off[CH];
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    const int pos = (wave * CH + r) * 64 + lane;  // chunk slot in the tile
+    const int row = pos / CPR, slot = pos % CPR;
+    krow_c[r] = row;
+    lane_off[r] = (uint32_t)row * sn2 + (uint32_t)((slot ^ swz(row)) * 16);
+  }
+  const int win_len = tr.k[0].row_len;  // window mode: keys per window row
+  const uint32_t wrap_add = (uint32_t)(tr.k[0].pitch - tr.k[0].row_len) * sn2;
+  const uint32_t step_bytes = (uint32_t)kBN * sn2;
+  int cur_run = 0, cur_left = 0, cur_off = 0, cur_c0 = 0;
+  uint32_t cur_base = 0;
+  auto cursor_reset = [&]() __attribute__((always_inline)) {
+    cur_run = 0;
+    cur_left = tr.nk[0];
+    cur_off = 0;
+    cur_c0 = 0;
+    cur_base = (uint32_t)tr.k[0].start * sn2;
+  };
+  auto cursor_next = [&]() __attribute__((always_inline)) {
+    cur_left -= kBN;
+    cur_off += kBN;
+    if (MODE == NPA_MODE_STRIPS && cur_left <= 0) {
+      // next non-empty key run (the stale halos)
+      cur_run = (cur_run == 0 && tr.nk[1] > 0) ? 1 : 2;
+      cur_left = cur_run == 1 ? tr.nk[1] : tr.nk[2];
+      cur_off = 0;
+      cur_base = (uint32_t)(cur_run == 1 ? tr.k[1].start : tr.k[2].start) * sn2;
+    } else {
+      cur_base += step_bytes;
+      if (MODE == NPA_MODE_WINDOW) {
+        cur_c0 += kBN;
+        while (cur_c0 >= win_len) {
+          cur_c0 -= win_len;
+          cur_base += wrap_add;
+        }
+      }
+    }
+  };
+  // Copies of the block the cursor is on: 2*CH buffer_load ... lds per wave
+  // (the K and the V chunk of each of its CH chunk slots); fetch_offsets
+  // computes the lanes' source offsets once per block.
+  auto fetch_offsets = [&](uint32_t (&off)[CH]) __attribute__((always_inline)) {
+    const bool general = MODE == NPA_MODE_WINDOW && win_len < 32;
+    const int lim1 = MODE == NPA_MODE_WINDOW ? win_len - cur_c0 : kBN;
+    const int lim2 = MODE == NPA_MODE_WINDOW ? lim1 + win_len : kBN;
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      const int inst = wave * CH + r;
-      const int pos = inst * 64 + lane;  // chunk slot in the tile
-      const int row = pos / CPR, slot = pos % CPR;
-      uint32_t off = kOOB;
-      if (row < bi.valid)
-        off = (uint32_t)run_token<MODE>(run, bi.off + row, inv_klen) * sn2 + (slot ^ swz(row)) * 16;
-      lds_ptr dk = (lds_ptr)&skd[inst * 512];
-      lds_ptr dv = (lds_ptr)&svd[inst * 512];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk, 16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dv, 16, off, 0, 0, 0);
+      const int row = krow_c[r];
+      if (general) {
+        // narrow windows: a block may cross more than two window rows
+        off[r] = kOOB;
+        if (row < cur_left)
+          off[r] = (uint32_t)run_token<MODE>(tr.k[0], cur_off + row, inv_klen) * sn2 + (lane_off[r] - (uint32_t)row * sn2);
+      } else {
+        off[r] = cur_base + lane_off[r];
+        if (MODE == NPA_MODE_WINDOW) off[r] += (row >= lim1 ? wrap_add : 0u) + (row >= lim2 ? wrap_add : 0u);
+        if (PARTIAL && row >= cur_left) off[r] = kOOB;
+      }
     }
+  };
+  auto fetch_part = [&](int r, bool is_v, uint32_t voff, __bf16* skd, __bf16* svd) __attribute__((always_inline)) {
+    // runs 1 and 2 are the stale halos; the descriptor is built from the chosen
+    // base pointer (a select between two descriptors would be lowered through memory)
+    const bool stale = MODE == NPA_MODE_STRIPS && cur_run != 0;
+    const __bf16* src = is_v ? (stale ? vs_base : vf_base) : (stale ? ks_base : kf_base);
+    const rsrc_t rs = make_rsrc(src, a.range_bytes);
+    lds_ptr dst = (lds_ptr)&(is_v ? svd : skd)[(wave * CH + r) * 512];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, 0, 0, 0);
+  };
+  auto fetch = [&](__bf16* skd, __bf16* svd) __attribute__((always_inline)) {
+    uint32_t off[CH];
+    fetch_offsets(off);
+#pragma unroll
+    for (int j = 0; j < 2 * CH; ++j) fetch_part(j >> 1, j & 1, off[j >> 1], skd, svd);
   };
 
   f32x16 o[DT][NT];
@@ -350,7 +390,11 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
     auto block = [&](int kb, const __bf16* skb, __bf16* skn, __bf16* svn) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
+      const int valid = cur_left;  // the cursor is on block kb
+      if (kb + 1 < nkb) {
+        cursor_next();
+        fetch(skn, svn);
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         f32x16 s[NT];
@@ -361,7 +405,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? f32x16{} : s[nt]);
         }
-        const int base = block_info(tr, kb).valid - mt * 32;
+        const int base = valid - mt * 32;
         const int t = base - 8 * g;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -370,7 +414,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
             for (int nt = 0; nt < NT; ++nt) mx[nt] = fmaxf(mx[nt], s[nt][j]);
       }
     };
-    fetch(0, sk0, sv0);
+    cursor_reset();
+    fetch(sk0, sv0);
     for (int kb = 0; kb < nkb; kb += 2) {
       block(kb, sk0, sk1, sv1);
       if (kb + 1 < nkb) block(kb + 1, sk1, sk0, sv0);
@@ -399,8 +444,11 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kb + 1 < nkb) fetch(kb + 1, skn, svn);
-    const int valid = MASK ? block_info(tr, kb).valid : kBN;
+    const int valid = MASK ? cur_left : kBN;  // the cursor is on block kb
+    if (kb + 1 < nkb) {
+      cursor_next();
+      fetch(skn, svn);
+    }
 
     // S^T of half mt (exp2 domain; shifted by -m unless FIRST)
     auto scores = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
@@ -461,7 +509,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
         scores(mt, s0);
         mask(mt, s0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s0[nt], pa0[nt], pa1[nt]);
+        for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[nt], pa0[nt], pa1[nt], l[nt]);
         pv(mt, pa0, pa1);
       }
       return;
@@ -474,7 +522,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float m = pair_max(max16(s0[nt]));
-        l[nt] += exp_pack(s0[nt], m, pa0[nt], pa1[nt]);
+        l[nt] = exp_pack(s0[nt], m, pa0[nt], pa1[nt], l[nt]);
 #pragma unroll
         for (int j = 0; j < 16; ++j) shift[nt][j] = -m;
       }
@@ -490,7 +538,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
       }
       mask(1, s1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s1[nt], pb0[nt], pb1[nt]);
+      for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
       pv(1, pb0, pb1);
       return;
     }
@@ -498,7 +546,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
     // half 1's score MFMAs run while the VALU turns half 0's scores into weights
     scores(1, s1);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s0[nt], pa0[nt], pa1[nt]);
+    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[nt], pa0[nt], pa1[nt], l[nt]);
 #pragma unroll
     for (int i = 0; i < kSMfma; ++i) {
       if (i < kSReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -511,7 +559,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
     // half 0's PV MFMAs run while the VALU does half 1's weights
     pv(0, pa0, pa1);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] += exp_pack0(s1[nt], pb0[nt], pb1[nt]);
+    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
 #pragma unroll
     for (int i = 0; i < kPVMfma; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, kPVReads / kPVMfma, 0);  // DS read
@@ -523,7 +571,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
   };
   // block kb of the pass, picking the body for partial blocks at run time
   auto any_block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn) __attribute__((always_inline)) {
-    if (PARTIAL && block_info(tr, kb).valid < kBN)
+    if (PARTIAL && cur_left < kBN)
       block(kb, skb, svb, skn, svn, std::false_type{}, std::integral_constant<bool, PARTIAL>{});
     else
       block(kb, skb, svb, skn, svn, std::false_type{}, std::false_type{});
@@ -535,10 +583,11 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
       for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x16{};
       l[nt] = 0.0f;
     }
-    fetch(0, sk0, sv0);
+    cursor_reset();
+    fetch(sk0, sv0);
     if (preset)
       any_block(0, sk0, sv0, sk1, sv1);
-    else if (PARTIAL && block_info(tr, 0).valid < kBN)
+    else if (PARTIAL && cur_left < kBN)
       block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::integral_constant<bool, PARTIAL>{});
     else
       block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::false_type{});
@@ -599,14 +648,14 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::MINB) void attn_bf16_kernel(const
 }  // namespace
 
 int attn_bf16_block_m(int head_dim) {
-  if (head_dim == 64) return kWaves * 32 * Cfg<64>::NT;
-  if (head_dim == 128) return kWaves * 32 * Cfg<128>::NT;
+  if (head_dim == 64) return Cfg<64>::WAVES * 32 * Cfg<64>::NT;
+  if (head_dim == 128) return Cfg<128>::WAVES * 32 * Cfg<128>::NT;
   return 0;
 }
 
 template <int D, int MODE>
 void launch_dm(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid(a.nblocks), block(kThreads);
+  const dim3 grid(a.nblocks), block(64 * Cfg<D>::WAVES);
   if (a.partial)
     hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, true>), grid, block, 0, st, a);
   else
