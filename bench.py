@@ -2,14 +2,18 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: the partial-attention layer call (npa_attn_fwd) and
-the structure-guidance blend (npa_sg_blend) of the workload.  W untimed warm-up
-steps, then K steps timed with HIP events on the stream the kernels run on.
+the structure-guidance blend (npa_sg_blend) of the workload.  First --settle
+seconds of back-to-back steps (the GPU's clock governor raises the shader
+clock over a second or two of sustained load), then W untimed warm-up steps,
+then K steps timed with HIP events on the stream the kernels run on.
 
 The JSON line carries:
   value     -- useful attention flops per step / step time (TFLOP/s);
   roofline  -- the attention kernel alone: useful flops / its average launch
                duration (HIP events around each launch), against the dense
-               bf16 MFMA peak;
+               bf16 MFMA peak at 2.4 GHz; sclk_mhz / power_w are the shader
+               clock and board power sampled from sysfs during the timed
+               steps, frac_at_sclk the fraction of the peak at that clock;
   cpu_baseline -- the fp64 oracle timed on a bounded sample of the same
                workload on this host's cores (rank 0, N=1 only).
 """
@@ -75,10 +79,13 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdxl4096_npa")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--settle", type=float, default=3.0,
+                    help="seconds of back-to-back steps before the warm-up steps, so that the GPU's clock "
+                         "governor has raised the shader clock to its sustained level (it ramps over ~1-2 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (outside the timed region) so that a "
@@ -93,7 +100,7 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from partial_context_patch_amd import npa
+    from partial_context_patch_amd import npa, profiling
     from partial_context_patch_amd import workloads as WL
 
     npa.load(build_if_missing=False)
@@ -134,12 +141,27 @@ def main() -> int:
         torch.cuda.synchronize()
         log("calibration copy: 512 MiB read + 512 MiB written")
         del src, dst
+    # settle: the shader clock ramps up over a second or two of sustained load; a
+    # diffusion sampler keeps the GPU busy for far longer than that, so steps are
+    # timed at the sustained clock
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            step()
+        n_settle += 10
+        torch.cuda.synchronize()
+    if args.settle > 0:
+        log(f"settled the clock with {n_settle} steps in {time.perf_counter() - t_settle:.1f} s")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # the GPU's shader clock and board power, sampled from sysfs while the timed
+    # steps run
+    sampler = profiling.ClockSampler().start()
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
@@ -147,6 +169,8 @@ def main() -> int:
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    sampler.stop()
+    clock = sampler.summary()
     ms_step = start.elapsed_time(stop) / args.steps
     attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     sg_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -158,8 +182,8 @@ def main() -> int:
     achieved = flops / (attn_avg * 1e-3) / 1e12
     # structure-guidance blend: reads x and ref, writes out, 4 bytes each per element
     sg_bytes = 12 * sgw["channels"] * sgw["map_h"] * sgw["map_w"]
-    from partial_context_patch_amd import profiling
     traffic = profiling.load_traffic(name)
+    sclk = clock.get("sclk_mhz")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -180,6 +204,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -191,7 +216,10 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else int(traffic),
-                     "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg, 5)},
+                     "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg, 5),
+                     "sclk_mhz": sclk, "sclk_samples": clock["sclk_samples"],
+                     "power_w": clock["power_w"], "power_cap_w": clock["power_cap_w"],
+                     "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4)},
         "sg_blend": {"bound": "hbm", "achieved": round(sg_bytes / (sg_avg * 1e-3) / 1e9, 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(sg_bytes / (sg_avg * 1e-3) / 1e9 / 8000.0, 4),
                      "algorithmic_bytes": sg_bytes, "avg_launch_ms": round(sg_avg, 5)},

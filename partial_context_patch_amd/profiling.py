@@ -120,6 +120,58 @@ def load_traffic(workload: str) -> Optional[float]:
     return None
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (the starred level of
+    pp_dpm_sclk, in MHz) and board power (hwmon power1_input, in W) from sysfs
+    on a background thread, every `period` seconds, between start() and stop().
+    Reads only; when the files are absent the results are None."""
+
+    def __init__(self, period: float = 0.002):
+        import threading
+        self.period = period
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        dev = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self._sclk_path = dev[0] if dev else None
+        hw = sorted(glob.glob(os.path.join(os.path.dirname(dev[0]), "hwmon", "hwmon*", "power1_input"))) if dev else []
+        self._power_path = hw[0] if hw else None
+        cap = os.path.join(os.path.dirname(hw[0]), "power1_cap") if hw else None
+        self.power_cap_w = None
+        if cap and os.path.exists(cap):
+            try:
+                self.power_cap_w = int(open(cap).read()) / 1e6
+            except (OSError, ValueError):
+                pass
+
+    def _run(self):
+        import time
+        while not self._stop.is_set():
+            try:
+                if self._sclk_path:
+                    for line in open(self._sclk_path):
+                        if line.rstrip().endswith("*"):
+                            self.sclk.append(float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0]))
+                if self._power_path:
+                    self.power.append(int(open(self._power_path).read()) / 1e6)
+            except (OSError, ValueError, IndexError):
+                pass
+            time.sleep(self.period)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self) -> dict:
+        mean = lambda v: round(statistics.fmean(v), 1) if v else None
+        return {"sclk_mhz": mean(self.sclk), "sclk_samples": len(self.sclk), "power_w": mean(self.power),
+                "power_cap_w": self.power_cap_w}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
