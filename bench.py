@@ -47,7 +47,7 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
     from partial_context_patch_amd import workloads as WL
 
     w = WL.ATTENTION_WORKLOADS[name]
-    spec = (A.Strips(w["num_strips"], p=w["p"]) if w["mode"] == "strips"
+    spec = (A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows")) if w["mode"] == "strips"
             else A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"]))
     H, W, d = w["map_h"], w["map_w"], w["head_dim"]
     tiles = list(A.iter_tiles(H, W, spec))
@@ -116,10 +116,7 @@ def main() -> int:
     x, ref = WL.sg_inputs(sgw["channels"], sgw["map_h"], sgw["map_w"], seed=sgw["seed"])
     x, ref = torch.from_numpy(x).to(dev), torch.from_numpy(ref).to(dev)
     sg_out = torch.empty_like(x)
-    if w["mode"] == "strips":
-        kw = dict(strips=w["num_strips"], p=w["p"])
-    else:
-        kw = dict(tile=(w["tile_h"], w["tile_w"]), halo=(w["halo_h"], w["halo_w"]))
+    kw = WL.halo_kwargs(w)
     L = npa.make_layout(w["batch"], w["heads"], w["head_dim"], w["map_h"], w["map_w"], dtype=w["dtype"])
     flops = npa.useful_flops(L, npa.make_halo(**kw))
     hw = (w["map_h"], w["map_w"])
@@ -194,7 +191,7 @@ def main() -> int:
            "head_dim": w["head_dim"], "map": f"{w['map_h']}x{w['map_w']}",
            "useful_gflop_per_step": flops / 1e9, "sg_blend": sgw["what"]}
     if w["mode"] == "strips":
-        cfg.update(strips=w["num_strips"], p=w["p"])
+        cfg.update(strips=w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
     else:
         cfg.update(tile=f"{w['tile_h']}x{w['tile_w']}", halo=w["halo_h"])
     rec = {

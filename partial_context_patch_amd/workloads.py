@@ -45,6 +45,18 @@ ATTENTION_WORKLOADS: Dict[str, dict] = {
         tile_h=64, tile_w=64, halo_h=16, halo_w=16, dtype="bf16", seed=1004,
         what="SDXL 4096^2 first attention level, NPA: 256x256 tokens, 10x64 heads, 64x64 query tiles, 96x96 windows",
     ),
+    # Halo settings at their limits (DistriFusion's full stale context, the
+    # synchronous warm-up steps with full fresh attention): parity cases.
+    "sdxl2048_fullstale": dict(
+        mode="strips", batch=2, heads=10, head_dim=64, map_h=128, map_w=128,
+        num_strips=8, p=None, halo_rows=128, dtype="bf16", seed=1007,
+        what="SDXL 2048^2, 8 strips, full stale context: own strip fresh, every other row stale",
+    ),
+    "sdxl1024_warmup": dict(
+        mode="strips", batch=2, heads=10, head_dim=64, map_h=64, map_w=64,
+        num_strips=1, p=0.0, dtype="bf16", seed=1008,
+        what="SDXL 1024^2 warm-up step: one strip, full fresh attention",
+    ),
     "flux4096_npa": dict(
         mode="window", batch=1, heads=24, head_dim=128, map_h=256, map_w=256,
         tile_h=32, tile_w=32, halo_h=16, halo_w=16, dtype="bf16", seed=1005,
@@ -108,6 +120,14 @@ def attention_inputs(
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype}")
     return out
+
+
+def halo_kwargs(w: dict) -> dict:
+    """The workload's strip or window settings as keyword arguments of
+    npa.attn_fwd / npa.make_halo."""
+    if w["mode"] == "strips":
+        return dict(strips=w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
+    return dict(tile=(w["tile_h"], w["tile_w"]), halo=(w["halo_h"], w["halo_w"]))
 
 
 def workload_inputs(name: str) -> Dict[str, Optional[np.ndarray]]:

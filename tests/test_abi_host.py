@@ -107,11 +107,10 @@ def test_planner_matches_oracle(lib, H, W, kw):
 def test_useful_flops_of_workloads(lib, name):
     w = WL.ATTENTION_WORKLOADS[name]
     L = npa.make_layout(w["batch"], w["heads"], w["head_dim"], w["map_h"], w["map_w"], dtype=w["dtype"])
+    h = npa.make_halo(**WL.halo_kwargs(w))
     if w["mode"] == "strips":
-        h = npa.make_halo(strips=w["num_strips"], p=w["p"])
-        spec = A.Strips(w["num_strips"], p=w["p"])
+        spec = A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
     else:
-        h = npa.make_halo(tile=(w["tile_h"], w["tile_w"]), halo=(w["halo_h"], w["halo_w"]))
         spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
     assert npa.useful_flops(L, h) == A.useful_flops(w["batch"], w["heads"], w["head_dim"], w["map_h"], w["map_w"], spec)
 

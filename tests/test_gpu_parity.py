@@ -82,7 +82,7 @@ def test_explicit_scale_and_halo_beyond_map():
 # ------------------------------------------------------------- full sizes
 def _workload_spec(w):
     if w["mode"] == "strips":
-        return A.Strips(w["num_strips"], p=w["p"])
+        return A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
     return A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
 
 

@@ -71,7 +71,7 @@ def test_workload_counts():
         w = WL.ATTENTION_WORKLOADS[name]
         H, W = w["map_h"], w["map_w"]
         if w["mode"] == "strips":
-            spec = A.Strips(w["num_strips"], p=w["p"])
+            spec = A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
             assert A.halo_rows(H, spec) == g["halo_rows"]
         else:
             spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
