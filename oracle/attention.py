@@ -26,6 +26,11 @@ Membership (the two methods):
   non-overlapping th x tw query tiles; a query in tile (ti, tj) attends to the
   fresh keys of the rectangle grown by halo_h rows and halo_w columns on each
   side, clipped at the image border (the window shrinks; it is not shifted).
+* Windows with text tokens (FLUX's joint attention; the ScaleDiff page applies
+  NPA to FLUX but does not say how the prompt's tokens take part -- reading:
+  they are global).  The tensors hold T text tokens first, then the map's
+  tokens (map token t at index T + t).  A map query attends to its window and
+  to all T text tokens; a text query attends to every token, text and map.
 
 Two tiers that share no code with each other beyond the spec objects:
   tier 0 -- explicit Python loops over (q, k) with the per-pair predicate
@@ -58,12 +63,19 @@ class Strips:
 
 @dataclass(frozen=True)
 class Windows:
-    """Non-overlapping tile_h x tile_w query tiles with a (halo_h, halo_w) K/V halo."""
+    """Non-overlapping tile_h x tile_w query tiles with a (halo_h, halo_w) K/V halo;
+    text_tokens global tokens stored before the map's tokens."""
 
     tile_h: int
     tile_w: int
     halo_h: int
     halo_w: int
+    text_tokens: int = 0
+
+
+def text_tokens(spec) -> int:
+    """Global text tokens stored before the map's tokens (0 for strips)."""
+    return spec.text_tokens if isinstance(spec, Windows) else 0
 
 
 def strip_height(H: int, spec: Strips) -> int:
@@ -127,13 +139,17 @@ def pair_in_stale(H: int, W: int, spec, q_rc: Tuple[int, int], k_rc: Tuple[int, 
 
 
 def attended_sets(H: int, W: int, spec) -> list:
-    """For every query token t: (sorted fresh key tokens, sorted stale key tokens)."""
+    """For every stored token (text tokens first, then the map row-major):
+    (sorted fresh key indices, sorted stale key indices)."""
+    T = text_tokens(spec)
     out = []
+    for t in range(T):  # a text query sees everything
+        out.append((list(range(T + H * W)), []))
     for t in range(H * W):
         q_rc = divmod(t, W)
-        fr = [k for k in range(H * W) if pair_in_fresh(H, W, spec, q_rc, divmod(k, W))]
-        st = [k for k in range(H * W) if pair_in_stale(H, W, spec, q_rc, divmod(k, W))]
-        out.append((fr, st))
+        fr = [T + k for k in range(H * W) if pair_in_fresh(H, W, spec, q_rc, divmod(k, W))]
+        st = [T + k for k in range(H * W) if pair_in_stale(H, W, spec, q_rc, divmod(k, W))]
+        out.append((list(range(T)) + fr, st))
     return out
 
 
@@ -143,7 +159,7 @@ def attention_tier0(q, k, v, k_stale, v_stale, H: int, W: int, spec, scale: Opti
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, N, Hh, d = q.shape
-    assert N == H * W
+    assert N == text_tokens(spec) + H * W
     scale = default_scale(d) if scale is None else scale
     if k_stale is not None:
         k_stale = np.asarray(k_stale, dtype=np.float64)
@@ -180,7 +196,9 @@ def iter_tiles(H: int, W: int, spec) -> Iterator[Tuple[np.ndarray, np.ndarray, n
     """Yield (query tokens, fresh key tokens, stale key tokens) per query tile.
 
     Every token of the map belongs to exactly one tile; all queries of a tile
-    share one key set.  Selection is by predicate over all H*W tokens.
+    share one key set.  Selection is by predicate over all H*W tokens.  With
+    text tokens, indices are into the stored sequence (text first) and the
+    text queries form one more tile, last.
     """
     tok = np.arange(H * W)
     rows, cols = tok // W, tok % W
@@ -196,15 +214,20 @@ def iter_tiles(H: int, W: int, spec) -> Iterator[Tuple[np.ndarray, np.ndarray, n
             yield tok[qsel], tok[fsel], tok[ssel]
         return
     th, tw, eh, ew = spec.tile_h, spec.tile_w, spec.halo_h, spec.halo_w
+    T = spec.text_tokens
     if H % th or W % tw:
         raise ValueError("query tiles must divide the map")
+    text = np.arange(T)
+    empty = np.zeros(0, dtype=tok.dtype)
     for ti in range(H // th):
         for tj in range(W // tw):
             qsel = (rows // th == ti) & (cols // tw == tj)
             r_lo, r_hi = max(0, ti * th - eh), min(H, (ti + 1) * th + eh)
             c_lo, c_hi = max(0, tj * tw - ew), min(W, (tj + 1) * tw + ew)
             fsel = (rows >= r_lo) & (rows < r_hi) & (cols >= c_lo) & (cols < c_hi)
-            yield tok[qsel], tok[fsel], tok[np.zeros_like(fsel)]
+            yield T + tok[qsel], np.concatenate([T + tok[fsel], text]), empty
+    if T:
+        yield text, np.arange(T + H * W), empty
 
 
 def useful_pairs(H: int, W: int, spec) -> int:
@@ -247,7 +270,7 @@ def attention_tier1(
     Returns an fp64 array of shape [B, N, Hh, dv].
     """
     B, N, Hh, d = q.shape
-    assert N == H * W
+    assert N == text_tokens(spec) + H * W
     scale = default_scale(d) if scale is None else scale
     out = np.full((B, N, Hh, v.shape[-1]), np.nan)
     want = None

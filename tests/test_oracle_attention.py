@@ -21,7 +21,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def _spec(case):
     if case["mode"] == "strips":
         return A.Strips(case["num_strips"], p=case.get("p"), halo_rows=case.get("halo_rows"))
-    return A.Windows(case["tile_h"], case["tile_w"], case["halo_h"], case["halo_w"])
+    return A.Windows(case["tile_h"], case["tile_w"], case["halo_h"], case["halo_w"], case.get("text_tokens", 0))
 
 
 def _rand(shape, seed):
@@ -74,7 +74,7 @@ def test_workload_counts():
             spec = A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
             assert A.halo_rows(H, spec) == g["halo_rows"]
         else:
-            spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
+            spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"], w.get("text_tokens", 0))
         sizes = [len(ft) + len(st) for _, ft, st in A.iter_tiles(H, W, spec)]
         assert max(sizes) == g["keys_interior"] and min(sizes) == g["keys_border"], name
         assert A.useful_pairs(H, W, spec) == g["pairs_per_bh"], name
@@ -88,6 +88,41 @@ def test_one_strip_is_full_attention():
     for spec in (A.Strips(1, p=0.7), A.Windows(H, W, 0, 0), A.Windows(2, 1, 9, 9)):
         got = A.attention_tier1(q, k, v, ks, vs, H, W, spec)
         np.testing.assert_allclose(got, _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_joint_whole_map_window_is_full_attention(T):
+    """A window that covers the whole map makes every query, text or map, see
+    every stored token: plain attention over all T + N tokens."""
+    H, W, B, Hh, d = 4, 6, 2, 2, 8
+    N = T + H * W
+    q, k, v = (_rand((B, N, Hh, d), s) for s in (21 + T, 22 + T, 23 + T))
+    for spec in (A.Windows(H, W, 0, 0, T), A.Windows(2, 3, 9, 9, T)):
+        got = A.attention_tier1(q, k, v, None, None, H, W, spec)
+        np.testing.assert_allclose(got, _sdpa(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_joint_tiers_agree():
+    """Loop tier (per-pair predicates) against the vectorised tier on a joint case."""
+    H, W, B, Hh, d, T = 4, 4, 1, 2, 4, 3
+    N = T + H * W
+    q, k, v = (_rand((B, N, Hh, d), s) for s in (31, 32, 33))
+    spec = A.Windows(2, 2, 1, 1, T)
+    np.testing.assert_allclose(A.attention_tier1(q, k, v, None, None, H, W, spec),
+                               A.attention_tier0(q, k, v, None, None, H, W, spec), rtol=0, atol=1e-12)
+
+
+def test_joint_text_keys_are_reached():
+    """Map queries put weight on the text keys: with every map key's value 0 and
+    every text key's value 1, each map query's output is the softmax mass on the
+    text keys, in (0, 1); text queries see the same keys plus the rest of the map."""
+    H, W, B, Hh, d, T = 4, 4, 1, 1, 4, 2
+    N = T + H * W
+    q, k = _rand((B, N, Hh, d), 41), _rand((B, N, Hh, d), 42)
+    v = np.zeros((B, N, Hh, 1))
+    v[:, :T] = 1.0
+    out = A.attention_tier1(q, k, v, None, None, H, W, A.Windows(2, 2, 0, 0, T))
+    assert np.all(out > 0) and np.all(out < 1)
 
 
 def test_p0_is_block_diagonal():

@@ -21,7 +21,7 @@ def _golden_membership_holds() -> bool:
     for case in gold["cases"]:
         spec = (A.Strips(case["num_strips"], p=case.get("p"), halo_rows=case.get("halo_rows"))
                 if case["mode"] == "strips"
-                else A.Windows(case["tile_h"], case["tile_w"], case["halo_h"], case["halo_w"]))
+                else A.Windows(case["tile_h"], case["tile_w"], case["halo_h"], case["halo_w"], case.get("text_tokens", 0)))
         tiles = list(A.iter_tiles(case["H"], case["W"], spec))
         sets = A.attended_sets(case["H"], case["W"], spec)
         for exp, (qt, ft, st) in zip(case["tiles"], tiles):
@@ -118,3 +118,46 @@ def test_zero_padded_border_is_caught(monkeypatch):
     x = np.random.default_rng(2).standard_normal((1, 30, 30))
     ref = ndi.gaussian_filter(x, sigma=4.0, mode="mirror", truncate=3.0, axes=(1, 2))
     assert not np.allclose(G.lowpass(x, 4.0), ref, atol=1e-6)
+
+
+def test_text_keys_dropped_for_map_queries_is_caught(monkeypatch):
+    """Map queries attend to their window only (text keys left out)."""
+    orig = A.iter_tiles
+
+    def bad(H, W, spec):
+        T = A.text_tokens(spec)
+        for qt, ft, st in orig(H, W, spec):
+            if T and qt.min() >= T:
+                ft = ft[ft >= T]
+            yield qt, ft, st
+    monkeypatch.setattr(A, "iter_tiles", bad)
+    assert not _golden_membership_holds()
+
+
+def test_text_queries_windowed_is_caught(monkeypatch):
+    """Text queries attend to the text tokens only."""
+    orig = A.iter_tiles
+
+    def bad(H, W, spec):
+        T = A.text_tokens(spec)
+        for qt, ft, st in orig(H, W, spec):
+            if T and qt.max() < T:
+                ft = ft[ft < T]
+            yield qt, ft, st
+    monkeypatch.setattr(A, "iter_tiles", bad)
+    assert not _golden_membership_holds()
+
+
+def test_map_tokens_not_offset_is_caught(monkeypatch):
+    """Map tokens indexed from 0 (as if no text tokens were stored before them)."""
+    orig = A.iter_tiles
+
+    def bad(H, W, spec):
+        T = A.text_tokens(spec)
+        for qt, ft, st in orig(H, W, spec):
+            if T and qt.min() >= T:
+                qt = qt - T
+                ft = np.concatenate([ft[ft >= T] - T, ft[ft < T]])
+            yield qt, ft, st
+    monkeypatch.setattr(A, "iter_tiles", bad)
+    assert not _golden_membership_holds()
