@@ -48,7 +48,7 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
 
     w = WL.ATTENTION_WORKLOADS[name]
     spec = (A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows")) if w["mode"] == "strips"
-            else A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"]))
+            else A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"], w.get("text_tokens", 0)))
     H, W, d = w["map_h"], w["map_w"], w["head_dim"]
     tiles = list(A.iter_tiles(H, W, spec))
     done_pairs, n_tiles, t0 = 0, 0, time.perf_counter()

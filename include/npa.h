@@ -24,6 +24,11 @@
  *     [max(0, ti*tile_h - halo_h), min(map_h, (ti+1)*tile_h + halo_h)) x cols
  *     [max(0, tj*tile_w - halo_w), min(map_w, (tj+1)*tile_w + halo_w)),
  *     i.e. the window is clipped (not shifted) at the border.
+ *     Joint attention (FLUX): with text_tokens = T > 0 the tensors hold T
+ *     text tokens first, then the map's tokens (map token t at index T + t).
+ *     The same page applies NPA to FLUX without saying how the prompt's tokens
+ *     take part; reading: they are global -- a map query also attends to all
+ *     T text tokens, and a text query attends to every token, text and map.
  *
  * Attention itself (the multi-head scaled dot-product attention named in the
  * PCPP review's minor comment on Sec. 3.3):
@@ -63,10 +68,11 @@ typedef enum { NPA_MODE_STRIPS = 0, NPA_MODE_WINDOW = 1 } npa_mode_t;
 /* Shape and layout shared by Q, K_fresh, V_fresh, K_stale, V_stale and out.
  * Element (b, token t, head j, channel e) lives at
  *   base + b*stride_b + t*stride_n + j*stride_h + e        (elements)
- * with tokens row-major over the map, t = r*map_w + c.  Every pointer must be
- * 16-byte aligned and stride_b/stride_n/stride_h must keep each head's row
- * 16-byte aligned.  Limits: map_h*map_w <= 2^24, batch*heads*tiles*blocks
- * < 2^31. */
+ * with tokens row-major over the map, t = r*map_w + c (after the halo's
+ * text_tokens, when there are any: t = text_tokens + r*map_w + c).  Every
+ * pointer must be 16-byte aligned and stride_b/stride_n/stride_h must keep
+ * each head's row 16-byte aligned.  Limits: text_tokens + map_h*map_w <= 2^24,
+ * batch*heads*tiles*blocks < 2^31. */
 typedef struct {
   int32_t batch, heads, head_dim; /* head_dim: 64 or 128 for bf16; 32/64/128 for f32 */
   int32_t map_h, map_w;
@@ -85,6 +91,8 @@ typedef struct {
   /* window */
   int32_t tile_h, tile_w; /* must divide map_h, map_w */
   int32_t halo_h, halo_w; /* >= 0 */
+  int32_t text_tokens;    /* window mode: global text tokens stored before the
+                             map's tokens (>= 0; strips mode requires 0) */
 } npa_halo_t;
 
 /* One contiguous-by-rows run of tokens: `rows` runs of `row_len` tokens, the
@@ -94,7 +102,10 @@ typedef struct {
   int32_t start, row_len, rows, pitch;
 } npa_segment_t;
 
-/* The plan of one query tile: its query tokens and up to three key runs. */
+/* The plan of one query tile: its query tokens and up to three key runs.
+ * With text tokens the last tile holds the text queries (one run of T
+ * tokens, keys: every stored token) and each map tile has the text tokens as
+ * an extra key run. */
 typedef struct {
   npa_segment_t queries;   /* src is 0 */
   int32_t n_segments;      /* 1..3 */

@@ -47,9 +47,10 @@ npa_status_t make_geo(const npa_layout_t* L, const npa_halo_t* h, npa::Geo* g) {
   if (!L || !h) return fail(NPA_ERR_INVALID_ARG, "layout and halo must not be NULL");
   if (L->batch < 1 || L->heads < 1 || L->head_dim < 1 || L->map_h < 1 || L->map_w < 1)
     return fail(NPA_ERR_SHAPE, "batch, heads, head_dim, map_h, map_w must be >= 1");
-  if ((int64_t)L->map_h * L->map_w > (int64_t(1) << 24))
-    return fail(NPA_ERR_SHAPE, "map_h*map_w = %lld exceeds 2^24 tokens",
-                (long long)L->map_h * L->map_w);
+  if (h->text_tokens < 0) return fail(NPA_ERR_SHAPE, "text_tokens=%d must be >= 0", h->text_tokens);
+  if ((int64_t)h->text_tokens + (int64_t)L->map_h * L->map_w > (int64_t(1) << 24))
+    return fail(NPA_ERR_SHAPE, "text_tokens + map_h*map_w = %lld exceeds 2^24 tokens",
+                (long long)h->text_tokens + (long long)L->map_h * L->map_w);
   std::memset(g, 0, sizeof *g);
   g->mode = h->mode;
   g->H = L->map_h;
@@ -67,7 +68,10 @@ npa_status_t make_geo(const npa_layout_t* L, const npa_halo_t* h, npa::Geo* g) {
       g->h = halo_from_p(h->p, g->s);
     }
     if (g->h > L->map_h) g->h = L->map_h;  // a longer halo reads nothing more
-    g->n_tiles = h->num_strips;
+    if (h->text_tokens != 0)
+      return fail(NPA_ERR_UNSUPPORTED, "text tokens are supported in window mode only");
+    g->n_img = h->num_strips;
+    g->n_tiles = g->n_img;
   } else if (h->mode == NPA_MODE_WINDOW) {
     if (h->tile_h < 1 || h->tile_w < 1 || L->map_h % h->tile_h || L->map_w % h->tile_w)
       return fail(NPA_ERR_SHAPE, "tile %dx%d must be >= 1 and divide the %dx%d map", h->tile_h,
@@ -79,7 +83,9 @@ npa_status_t make_geo(const npa_layout_t* L, const npa_halo_t* h, npa::Geo* g) {
     g->eh = h->halo_h < L->map_h ? h->halo_h : L->map_h;
     g->ew = h->halo_w < L->map_w ? h->halo_w : L->map_w;
     g->tiles_x = L->map_w / h->tile_w;
-    g->n_tiles = (L->map_h / h->tile_h) * g->tiles_x;
+    g->T = h->text_tokens;
+    g->n_img = (L->map_h / h->tile_h) * g->tiles_x;
+    g->n_tiles = g->n_img + (g->T > 0 ? 1 : 0);
   } else {
     return fail(NPA_ERR_INVALID_ARG, "unknown mode %d", h->mode);
   }
@@ -107,25 +113,25 @@ bool has_partial_blocks(const npa::Geo& g) {
 bool reads_stale(const npa::Geo& g) {
   for (int32_t t = 0; t < g.n_tiles; ++t) {
     const npa::TileRuns r = npa::tile_runs(g, t);
-    if (r.nk[1] + r.nk[2] > 0) return true;
+    for (int i = 0; i < 3; ++i)
+      if (r.src[i] == 1 && r.nk[i] > 0) return true;
   }
   return false;
 }
 
-// [lo, hi) byte extent of one tensor under the layout.
-void extent(const void* p, const npa_layout_t* L, int64_t esize, uintptr_t* lo, uintptr_t* hi) {
-  const int64_t N = (int64_t)L->map_h * L->map_w;
+// [lo, hi) byte extent of one tensor of N stored tokens under the layout.
+void extent(const void* p, const npa_layout_t* L, int64_t N, int64_t esize, uintptr_t* lo, uintptr_t* hi) {
   const int64_t last = (int64_t)(L->batch - 1) * L->stride_b + (N - 1) * L->stride_n +
                        (int64_t)(L->heads - 1) * L->stride_h + L->head_dim;
   *lo = reinterpret_cast<uintptr_t>(p);
   *hi = *lo + (uintptr_t)(last * esize);
 }
 
-bool overlaps(const void* a, const void* b, const npa_layout_t* L, int64_t esize) {
+bool overlaps(const void* a, const void* b, const npa_layout_t* L, int64_t N, int64_t esize) {
   if (!a || !b) return false;
   uintptr_t a0, a1, b0, b1;
-  extent(a, L, esize, &a0, &a1);
-  extent(b, L, esize, &b0, &b1);
+  extent(a, L, N, esize, &a0, &a1);
+  extent(b, L, N, esize, &b0, &b1);
   return a0 < b1 && b0 < a1;
 }
 
@@ -203,10 +209,11 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
                 (long long)vec);
   if (L->stride_n < (int64_t)L->heads * L->head_dim && L->stride_h < L->head_dim)
     return fail(NPA_ERR_INVALID_ARG, "strides overlap heads");
+  const int64_t tokens = (int64_t)g.T + (int64_t)L->map_h * L->map_w;  // stored per (batch, head)
   for (const void* p : ins)
-    if (overlaps(out, p, L, esize)) return fail(NPA_ERR_INVALID_ARG, "out must not alias an input");
+    if (overlaps(out, p, L, tokens, esize)) return fail(NPA_ERR_INVALID_ARG, "out must not alias an input");
 
-  const int64_t range = ((int64_t)L->map_h * L->map_w - 1) * L->stride_n * esize + (int64_t)L->head_dim * esize;
+  const int64_t range = (tokens - 1) * L->stride_n * esize + (int64_t)L->head_dim * esize;
   if (L->dtype == NPA_BF16 && range > 0x7FFFFFF0ll)
     return fail(NPA_ERR_UNSUPPORTED,
                 "one (batch, head) slice spans %lld bytes; the bf16 kernel addresses at most 2^31-16",
@@ -228,10 +235,13 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   a.g = g;
   const int32_t nq = npa::tile_queries(g);
   a.qblocks = (nq + block_m - 1) / block_m;
-  const int64_t nblocks = (int64_t)L->batch * L->heads * g.n_tiles * a.qblocks;
+  a.text_qblocks = (g.T + block_m - 1) / block_m;
+  const int64_t text_blocks = (int64_t)L->batch * L->heads * a.text_qblocks;
+  const int64_t nblocks = text_blocks + (int64_t)L->batch * L->heads * g.n_img * a.qblocks;
   if (nblocks >= (int64_t(1) << 31))
     return fail(NPA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)nblocks);
   a.nblocks = (int32_t)nblocks;
+  a.text_blocks = (int32_t)text_blocks;
   float scale = L->scale;
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L->head_dim));
   if (!std::isfinite(scale)) return fail(NPA_ERR_INVALID_ARG, "scale must be finite");

@@ -93,15 +93,6 @@ struct Cfg<128> {
   static constexpr int MINB = 8 / WAVES;
 };
 
-// Blocks are dealt to the 8 XCDs round-robin; remap so that each XCD runs one
-// contiguous range of logical blocks (all query blocks of a tile share the
-// tile's K/V through that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  const int per = n >> 3, rem = n & 7;
-  const int x = i & 7, k = i >> 3;
-  return (x < rem) ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
-}
-
 // j / d for 0 <= j < 2^24 via a float reciprocal and one correction step.
 __device__ __forceinline__ int fast_div(int j, int d, float inv) {
   int q = (int)((float)j * inv);
@@ -199,8 +190,15 @@ __device__ __forceinline__ float max16(const f32x16& a) {
 
 // PARTIAL: some key run of the plan is not a multiple of 64 keys, so some
 // blocks end inside the padding and need masking (instantiated only then).
+// Kernel modes: strips, windows, and windows with text tokens (joint
+// attention; a separate instantiation so that plain windows keep the
+// single-run cursor).
+constexpr int kModeJoint = 2;
+
 template <int D, int MODE, bool PARTIAL>
 __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_kernel(const AttnArgs a) {
+  constexpr bool kWin = MODE != NPA_MODE_STRIPS;  // map tiles are 2-D windows
+  constexpr bool kRuns = MODE != NPA_MODE_WINDOW;  // more than one key run per tile
   constexpr int kWaves = Cfg<D>::WAVES;
   constexpr int kThreads = 64 * kWaves;
   constexpr int NT = Cfg<D>::NT;
@@ -226,13 +224,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
 
-  const int bid = xcd_remap(blockIdx.x, a.nblocks);
-  const int qb = bid % a.qblocks;
-  int rest = bid / a.qblocks;
-  const int tile = rest % a.g.n_tiles;
-  rest /= a.g.n_tiles;
-  const int head = rest % a.Hh;
-  const int b = rest / a.Hh;
+  const BlockCoord bc = decode_block(a, blockIdx.x, true);
+  const int qb = bc.qb, tile = bc.tile, head = bc.head, b = bc.b;
 
   const TileRuns tr = tile_runs(a.g, tile);
   const int nq = tr.q.count();
@@ -301,33 +294,40 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
     krow_c[r] = row;
     lane_off[r] = (uint32_t)row * sn2 + (uint32_t)((slot ^ swz(row)) * 16);
   }
-  const int win_len = tr.k[0].row_len;  // window mode: keys per window row
+  // Window mode: run 0 is the window (rows of cur_len keys, pitch apart) or,
+  // in the text tile, every stored token; run 1 is the text tokens.  A run
+  // of one row, and every run after the first, is contiguous: cur_len is then
+  // kContig and the block never crosses a row.
+  constexpr int kContig = 1 << 29;
   const uint32_t wrap_add = (uint32_t)(tr.k[0].pitch - tr.k[0].row_len) * sn2;
   const uint32_t step_bytes = (uint32_t)kBN * sn2;
-  int cur_run = 0, cur_left = 0, cur_off = 0, cur_c0 = 0;
+  int cur_run = 0, cur_left = 0, cur_off = 0, cur_c0 = 0, cur_len = kContig;
   uint32_t cur_base = 0;
   auto cursor_reset = [&]() __attribute__((always_inline)) {
     cur_run = 0;
     cur_left = tr.nk[0];
     cur_off = 0;
     cur_c0 = 0;
+    cur_len = (kWin && tr.k[0].rows > 1) ? tr.k[0].row_len : kContig;
     cur_base = (uint32_t)tr.k[0].start * sn2;
   };
   auto cursor_next = [&]() __attribute__((always_inline)) {
     cur_left -= kBN;
     cur_off += kBN;
-    if (MODE == NPA_MODE_STRIPS && cur_left <= 0) {
-      // next non-empty key run (the stale halos)
+    if (kRuns && cur_left <= 0) {
+      // next non-empty key run (strips: the stale halos; joint: the text tokens)
       cur_run = (cur_run == 0 && tr.nk[1] > 0) ? 1 : 2;
       cur_left = cur_run == 1 ? tr.nk[1] : tr.nk[2];
       cur_off = 0;
+      cur_c0 = 0;
+      cur_len = kContig;
       cur_base = (uint32_t)(cur_run == 1 ? tr.k[1].start : tr.k[2].start) * sn2;
     } else {
       cur_base += step_bytes;
-      if (MODE == NPA_MODE_WINDOW) {
+      if (kWin) {
         cur_c0 += kBN;
-        while (cur_c0 >= win_len) {
-          cur_c0 -= win_len;
+        while (cur_c0 >= cur_len) {
+          cur_c0 -= cur_len;
           cur_base += wrap_add;
         }
       }
@@ -337,20 +337,20 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
   // (the K and the V chunk of each of its CH chunk slots); fetch_offsets
   // computes the lanes' source offsets once per block.
   auto fetch_offsets = [&](uint32_t (&off)[CH]) __attribute__((always_inline)) {
-    const bool general = MODE == NPA_MODE_WINDOW && win_len < 32;
-    const int lim1 = MODE == NPA_MODE_WINDOW ? win_len - cur_c0 : kBN;
-    const int lim2 = MODE == NPA_MODE_WINDOW ? lim1 + win_len : kBN;
+    const bool general = kWin && cur_len < 32;
+    const int lim1 = kWin ? cur_len - cur_c0 : kBN;
+    const int lim2 = kWin ? lim1 + cur_len : kBN;
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
       const int row = krow_c[r];
       if (general) {
-        // narrow windows: a block may cross more than two window rows
+        // narrow windows (run 0 only): a block may cross more than two window rows
         off[r] = kOOB;
         if (row < cur_left)
           off[r] = (uint32_t)run_token<MODE>(tr.k[0], cur_off + row, inv_klen) * sn2 + (lane_off[r] - (uint32_t)row * sn2);
       } else {
         off[r] = cur_base + lane_off[r];
-        if (MODE == NPA_MODE_WINDOW) off[r] += (row >= lim1 ? wrap_add : 0u) + (row >= lim2 ? wrap_add : 0u);
+        if (kWin) off[r] += (row >= lim1 ? wrap_add : 0u) + (row >= lim2 ? wrap_add : 0u);
         if (PARTIAL && row >= cur_left) off[r] = kOOB;
       }
     }
@@ -663,16 +663,21 @@ void launch_dm(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int /*block_m*/, hipStream_t st) {
+  const int mode = a.g.mode == NPA_MODE_STRIPS ? NPA_MODE_STRIPS : (a.g.T > 0 ? kModeJoint : NPA_MODE_WINDOW);
   if (head_dim == 64) {
-    if (a.g.mode == NPA_MODE_STRIPS)
+    if (mode == NPA_MODE_STRIPS)
       launch_dm<64, NPA_MODE_STRIPS>(a, st);
-    else
+    else if (mode == NPA_MODE_WINDOW)
       launch_dm<64, NPA_MODE_WINDOW>(a, st);
-  } else {
-    if (a.g.mode == NPA_MODE_STRIPS)
-      launch_dm<128, NPA_MODE_STRIPS>(a, st);
     else
+      launch_dm<64, kModeJoint>(a, st);
+  } else {
+    if (mode == NPA_MODE_STRIPS)
+      launch_dm<128, NPA_MODE_STRIPS>(a, st);
+    else if (mode == NPA_MODE_WINDOW)
       launch_dm<128, NPA_MODE_WINDOW>(a, st);
+    else
+      launch_dm<128, kModeJoint>(a, st);
   }
   return hipGetLastError();
 }

@@ -32,12 +32,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sv[BN * D];
 
   const int tid = threadIdx.x;
-  const int qb = blockIdx.x % a.qblocks;
-  int rest = blockIdx.x / a.qblocks;
-  const int tile = rest % a.g.n_tiles;
-  rest /= a.g.n_tiles;
-  const int head = rest % a.Hh;
-  const int b = rest / a.Hh;
+  const BlockCoord bc = decode_block(a, blockIdx.x, false);
+  const int qb = bc.qb, tile = bc.tile, head = bc.head, b = bc.b;
 
   const TileRuns tr = tile_runs(a.g, tile);
   const int nq = tr.q.count();

@@ -20,7 +20,9 @@ struct Geo {
   int32_t th, tw;    // window: query tile
   int32_t eh, ew;    // window: halo
   int32_t tiles_x;   // window: tiles per map row
-  int32_t n_tiles;
+  int32_t T;         // window: text tokens stored before the map's tokens
+  int32_t n_img;     // map tiles; the text tile (T > 0) is tile n_img
+  int32_t n_tiles;   // n_img, plus one when T > 0
 };
 
 // A run of tokens: `rows` runs of `row_len` tokens, first at `start`, `pitch` apart.
@@ -43,7 +45,9 @@ NPA_HD int32_t imin(int32_t a, int32_t b) { return a < b ? a : b; }
 // Partially conditioned attention (strips): strip i attends to its own rows
 // fresh, plus the h rows nearest to it above and below, stale.
 // Neighbourhood patch attention (window): tile (ti, tj) attends to its window
-// grown by (eh, ew) and clipped at the map border, fresh.
+// grown by (eh, ew) and clipped at the map border, fresh.  With T text tokens
+// (stored first; map token t at T + t) every map tile also attends to the text
+// tokens (run 1), and the text tile's T queries attend to every stored token.
 NPA_HD TileRuns tile_runs(const Geo& g, int32_t tile) {
   TileRuns t;
   if (g.mode == NPA_MODE_STRIPS) {
@@ -56,22 +60,32 @@ NPA_HD TileRuns tile_runs(const Geo& g, int32_t tile) {
     t.src[1] = 1;
     t.k[2] = Run{r1 * g.W, (b1 - r1) * g.W, 1, (b1 - r1) * g.W};
     t.src[2] = 1;
+  } else if (tile >= g.n_img) {
+    const int32_t all = g.T + g.H * g.W;
+    t.q = Run{0, g.T, 1, g.T};
+    t.k[0] = Run{0, all, 1, all};
+    t.src[0] = 0;
+    t.k[1] = Run{0, 0, 0, 0};
+    t.src[1] = 0;
+    t.k[2] = Run{0, 0, 0, 0};
+    t.src[2] = 0;
   } else {
     const int32_t ti = tile / g.tiles_x, tj = tile - ti * g.tiles_x;
     const int32_t r0 = imax(0, ti * g.th - g.eh), r1 = imin(g.H, (ti + 1) * g.th + g.eh);
     const int32_t c0 = imax(0, tj * g.tw - g.ew), c1 = imin(g.W, (tj + 1) * g.tw + g.ew);
-    t.q = Run{ti * g.th * g.W + tj * g.tw, g.tw, g.th, g.W};
-    t.k[0] = Run{r0 * g.W + c0, c1 - c0, r1 - r0, g.W};
+    t.q = Run{g.T + ti * g.th * g.W + tj * g.tw, g.tw, g.th, g.W};
+    t.k[0] = Run{g.T + r0 * g.W + c0, c1 - c0, r1 - r0, g.W};
     t.src[0] = 0;
-    t.k[1] = Run{0, 0, 0, 0};
-    t.src[1] = 1;
+    t.k[1] = Run{0, g.T, 1, g.T};
+    t.src[1] = 0;
     t.k[2] = Run{0, 0, 0, 0};
-    t.src[2] = 1;
+    t.src[2] = 0;
   }
   for (int i = 0; i < 3; ++i) t.nk[i] = t.k[i].count();
   return t;
 }
 
+// Queries of each map tile (strips or windows; the text tile has g.T).
 NPA_HD int32_t tile_queries(const Geo& g) {
   return g.mode == NPA_MODE_STRIPS ? g.s * g.W : g.th * g.tw;
 }
@@ -87,13 +101,53 @@ struct AttnArgs {
   int64_t sb, sn, sh;  // strides in elements
   int32_t B, Hh;
   Geo g;
-  int32_t qblocks;  // query blocks per tile
+  int32_t qblocks;  // query blocks per map tile
   int32_t nblocks;  // grid size
+  int32_t text_qblocks;  // query blocks of the text tile (0 without text tokens)
+  int32_t text_blocks;   // B * Hh * text_qblocks: the grid's first blocks
   float scale;      // softmax scale
   float c;          // scale * log2(e)
   uint32_t range_bytes;  // bytes spanned by one (batch, head) slice: ((N-1)*sn + d) * esize
   int32_t partial;       // some key run is not a multiple of 64 keys
 };
+
+// Which (query block, tile, head, batch) workgroup i of the grid computes.
+// The text tile's workgroups come first: each one walks every stored token,
+// many times the keys of a map tile, so they are started first (spread over
+// the XCDs by the hardware's round-robin) rather than left as a tail.  The map
+// tiles' workgroups follow; with `remap`, hardware ids are regrouped so that
+// each XCD runs one contiguous range of them (the query blocks of a tile, and
+// neighbouring tiles, share K/V through that XCD's L2).  Blocks are dealt to
+// the 8 XCDs round-robin, so the remap keeps each id's class mod 8.
+struct BlockCoord {
+  int32_t qb, tile, head, b;
+};
+
+NPA_HD int32_t xcd_remap(int32_t i, int32_t n) {
+  const int32_t per = n >> 3, rem = n & 7;
+  const int32_t x = i & 7, k = i >> 3;
+  return (x < rem) ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
+}
+
+NPA_HD BlockCoord decode_block(const AttnArgs& a, int32_t i, bool remap) {
+  BlockCoord c;
+  int32_t rest;
+  if (i < a.text_blocks) {
+    c.qb = i % a.text_qblocks;
+    rest = i / a.text_qblocks;
+    c.tile = a.g.n_img;
+  } else {
+    int32_t j = i - a.text_blocks;
+    if (remap) j = xcd_remap(j, a.nblocks - a.text_blocks);
+    c.qb = j % a.qblocks;
+    rest = j / a.qblocks;
+    c.tile = rest % a.g.n_img;
+    rest /= a.g.n_img;
+  }
+  c.head = rest % a.Hh;
+  c.b = rest / a.Hh;
+  return c;
+}
 
 // Arguments of the structure-guidance kernel.
 constexpr int kSgMaxRadius = 24;  // sigma <= 8; keeps the LDS tile under 64 KiB

@@ -41,6 +41,7 @@ class Halo(ctypes.Structure):
     _fields_ = [
         ("mode", c_int32), ("num_strips", c_int32), ("p", c_float), ("halo_rows", c_int32),
         ("tile_h", c_int32), ("tile_w", c_int32), ("halo_h", c_int32), ("halo_w", c_int32),
+        ("text_tokens", c_int32),
     ]
 
 
@@ -95,10 +96,13 @@ def _check(status: int):
 
 
 def make_halo(*, strips: Optional[int] = None, p: Optional[float] = None, halo_rows: Optional[int] = None,
-              tile: Optional[Tuple[int, int]] = None, halo: Optional[Tuple[int, int]] = None) -> Halo:
+              tile: Optional[Tuple[int, int]] = None, halo: Optional[Tuple[int, int]] = None,
+              text_tokens: int = 0) -> Halo:
     """strips=n with p or halo_rows (partially conditioned strips), or
-    tile=(th, tw) with halo=(eh, ew) (neighbourhood windows)."""
+    tile=(th, tw) with halo=(eh, ew) (neighbourhood windows), optionally with
+    text_tokens global tokens stored before the map's tokens."""
     h = Halo()
+    h.text_tokens = int(text_tokens)
     if strips is not None:
         if tile is not None:
             raise ValueError("give either strips or tile, not both")
@@ -161,11 +165,12 @@ def _stream_ptr(device) -> int:
 
 def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], strips: Optional[int] = None,
              p: Optional[float] = None, halo_rows: Optional[int] = None, tile: Optional[Tuple[int, int]] = None,
-             halo: Optional[Tuple[int, int]] = None, scale: Optional[float] = None, out=None):
+             halo: Optional[Tuple[int, int]] = None, text_tokens: int = 0, scale: Optional[float] = None, out=None):
     """Partial attention over device tensors [batch, tokens, heads, head_dim].
 
     All tensors share one dtype (bfloat16 or float32), one device and one set of
-    strides, with head_dim contiguous.  Returns `out` (allocated if None).
+    strides, with head_dim contiguous; tokens = text_tokens + map_h * map_w
+    (text tokens first).  Returns `out` (allocated if None).
     """
     import torch
 
@@ -174,8 +179,8 @@ def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], st
         raise ValueError("q must be [batch, tokens, heads, head_dim]")
     B, N, Hh, d = q.shape
     H, W = map_hw
-    if H * W != N:
-        raise ValueError(f"map {H}x{W} does not match {N} tokens")
+    if text_tokens + H * W != N:
+        raise ValueError(f"{text_tokens} text tokens and a {H}x{W} map do not match {N} tokens")
     dt = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(q.dtype)
     if dt is None:
         raise TypeError("q must be bfloat16 or float32")
@@ -190,7 +195,7 @@ def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], st
         if t.stride() != q.stride() or t.stride(-1) != 1:
             raise ValueError("all tensors must share q's strides with head_dim contiguous")
     L = make_layout(B, Hh, d, H, W, dtype=dt, strides=q.stride()[:3], scale=scale)
-    h = make_halo(strips=strips, p=p, halo_rows=halo_rows, tile=tile, halo=halo)
+    h = make_halo(strips=strips, p=p, halo_rows=halo_rows, tile=tile, halo=halo, text_tokens=text_tokens)
     ptr = lambda t: None if t is None else t.data_ptr()
     _check(lib.npa_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(k_stale), ptr(v_stale), ctypes.byref(L), ctypes.byref(h),
                             ptr(out), _stream_ptr(q.device)))

@@ -63,6 +63,15 @@ ATTENTION_WORKLOADS: Dict[str, dict] = {
         rms_qk=True,
         what="FLUX 4096^2 DiT, NPA: 256x256 packed tokens, 24x128 heads, 32x32 query tiles, 64x64 windows",
     ),
+    # FLUX's joint attention with the prompt's text tokens stored before the
+    # map's tokens (global: map queries also see every text token, text queries
+    # see everything).
+    "flux4096_joint": dict(
+        mode="window", batch=1, heads=24, head_dim=128, map_h=256, map_w=256,
+        tile_h=32, tile_w=32, halo_h=16, halo_w=16, text_tokens=512, dtype="bf16", seed=1009,
+        rms_qk=True,
+        what="FLUX 4096^2 joint attention: 512 text + 256x256 packed tokens, 24x128 heads, 32x32 query tiles, 64x64 windows",
+    ),
 }
 
 # Structure-guidance blend on the SDXL 4096^2 latent (4 channels, 512x512).
@@ -99,11 +108,13 @@ def attention_inputs(
     dtype: str = "bf16",
     stale: bool = True,
     rms_qk: bool = False,
+    text_tokens: int = 0,
     **_ignored,
 ) -> Dict[str, Optional[np.ndarray]]:
-    """Draw q, k, v (and k_stale, v_stale) as fp32 arrays of the storage values."""
+    """Draw q, k, v (and k_stale, v_stale) as fp32 arrays of the storage values;
+    with text tokens the sequence holds them first, then the map's tokens."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    shape = (batch, map_h * map_w, heads, head_dim)
+    shape = (batch, text_tokens + map_h * map_w, heads, head_dim)
     q = rng.standard_normal(shape, dtype=np.float32)
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
@@ -127,7 +138,7 @@ def halo_kwargs(w: dict) -> dict:
     npa.attn_fwd / npa.make_halo."""
     if w["mode"] == "strips":
         return dict(strips=w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
-    return dict(tile=(w["tile_h"], w["tile_w"]), halo=(w["halo_h"], w["halo_w"]))
+    return dict(tile=(w["tile_h"], w["tile_w"]), halo=(w["halo_h"], w["halo_w"]), text_tokens=w.get("text_tokens", 0))
 
 
 def workload_inputs(name: str) -> Dict[str, Optional[np.ndarray]]:

@@ -45,7 +45,8 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(npa_layout_t), offsetof(npa_layout_t, stride_b),
          offsetof(npa_layout_t, dtype), offsetof(npa_layout_t, scale), sizeof(npa_halo_t),
          sizeof(npa_segment_t), sizeof(npa_tile_desc_t));
-  printf("%zu %zu\n", offsetof(npa_halo_t, p), offsetof(npa_tile_desc_t, keys));
+  printf("%zu %zu %zu\n", offsetof(npa_halo_t, p), offsetof(npa_tile_desc_t, keys),
+         offsetof(npa_halo_t, text_tokens));
   return 0;
 }
 """
@@ -56,14 +57,14 @@ int main(void) {
         vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     L, H, S, T = npa.Layout, npa.Halo, npa.Segment, npa.TileDesc
     assert vals == [ctypes.sizeof(L), L.stride_b.offset, L.dtype.offset, L.scale.offset, ctypes.sizeof(H),
-                    ctypes.sizeof(S), ctypes.sizeof(T), H.p.offset, T.keys.offset]
+                    ctypes.sizeof(S), ctypes.sizeof(T), H.p.offset, T.keys.offset, H.text_tokens.offset]
 
 
 def _oracle_spec(h: npa.Halo):
     if h.mode == npa.NPA_MODE_STRIPS:
         return A.Strips(h.num_strips, p=h.p if h.halo_rows < 0 else None,
                         halo_rows=h.halo_rows if h.halo_rows >= 0 else None)
-    return A.Windows(h.tile_h, h.tile_w, h.halo_h, h.halo_w)
+    return A.Windows(h.tile_h, h.tile_w, h.halo_h, h.halo_w, h.text_tokens)
 
 
 def _run_tokens(seg):
@@ -83,6 +84,9 @@ CASES = [
     (40, 36, dict(tile=(40, 36), halo=(0, 0))),
     (40, 36, dict(tile=(4, 4), halo=(50, 50))),
     (16, 16, dict(tile=(1, 1), halo=(1, 0))),
+    (40, 36, dict(tile=(8, 12), halo=(5, 3), text_tokens=7)),
+    (16, 16, dict(tile=(4, 4), halo=(2, 2), text_tokens=64)),
+    (8, 8, dict(tile=(8, 8), halo=(0, 0), text_tokens=3)),
 ]
 
 
@@ -111,7 +115,7 @@ def test_useful_flops_of_workloads(lib, name):
     if w["mode"] == "strips":
         spec = A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
     else:
-        spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
+        spec = A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"], w.get("text_tokens", 0))
     assert npa.useful_flops(L, h) == A.useful_flops(w["batch"], w["heads"], w["head_dim"], w["map_h"], w["map_w"], spec)
 
 
@@ -149,6 +153,11 @@ def test_validation_errors(lib):
     assert _status(lib, zero, strips) == npa.NPA_ERR_SHAPE
     huge = npa.make_layout(1, 1, 64, 8192, 4096)
     assert _status(lib, huge, npa.make_halo(tile=(64, 64), halo=(0, 0))) == npa.NPA_ERR_SHAPE
+    # text tokens: window mode only, >= 0, within the token limit
+    assert _status(lib, good_L, npa.make_halo(strips=4, p=0.3, text_tokens=8)) == npa.NPA_ERR_UNSUPPORTED
+    assert _status(lib, good_L, npa.make_halo(tile=(8, 8), halo=(1, 1), text_tokens=-1)) == npa.NPA_ERR_SHAPE
+    big = npa.make_layout(1, 1, 64, 4096, 4096)
+    assert _status(lib, big, npa.make_halo(tile=(64, 64), halo=(0, 0), text_tokens=1)) == npa.NPA_ERR_SHAPE
     # unsupported head dim
     L96 = npa.make_layout(1, 2, 96, 32, 32)
     assert _status(lib, L96, strips) == npa.NPA_ERR_UNSUPPORTED
@@ -182,4 +191,9 @@ def test_window_mode_needs_no_stale(lib):
     tiles, _ = npa.plan(L, npa.make_halo(tile=(8, 8), halo=(4, 4)))
     assert all(s["src"] == 0 for t in tiles for s in t["keys"])
     tiles, _ = npa.plan(L, npa.make_halo(strips=4, p=0.0))
+    assert all(s["src"] == 0 for t in tiles for s in t["keys"])
+    # text tokens are fresh keys: a joint plan needs no stale pointers either
+    Lj = npa.make_layout(1, 2, 64, 32, 32)
+    hj = npa.make_halo(tile=(8, 8), halo=(4, 4), text_tokens=16)
+    tiles, _ = npa.plan(Lj, hj)
     assert all(s["src"] == 0 for t in tiles for s in t["keys"])

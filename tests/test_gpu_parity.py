@@ -31,7 +31,7 @@ def _dev(a, dt):
 def _kw(spec):
     if isinstance(spec, A.Strips):
         return dict(strips=spec.num_strips, p=spec.p, halo_rows=spec.halo_rows)
-    return dict(tile=(spec.tile_h, spec.tile_w), halo=(spec.halo_h, spec.halo_w))
+    return dict(tile=(spec.tile_h, spec.tile_w), halo=(spec.halo_h, spec.halo_w), text_tokens=spec.text_tokens)
 
 
 def _run(inp, H, W, spec, dt, scale=None):
@@ -56,13 +56,21 @@ SMALL = [
     (24, 20, 1, 2, 64, A.Strips(3, halo_rows=3), "f32"),
     (24, 20, 1, 2, 32, A.Strips(4, halo_rows=2), "f32"),
     (40, 36, 1, 2, 128, A.Windows(8, 12, 5, 3), "f32"),
+    # joint attention: text tokens stored before the map (ragged counts, a whole-map window)
+    (16, 16, 1, 2, 64, A.Windows(4, 4, 2, 2, 7), "bf16"),
+    (16, 12, 1, 2, 128, A.Windows(8, 4, 3, 2, 64), "bf16"),
+    (8, 8, 2, 2, 64, A.Windows(8, 8, 0, 0, 40), "bf16"),
+    (32, 32, 1, 1, 128, A.Windows(16, 16, 8, 8, 200), "bf16"),
+    (12, 8, 1, 2, 64, A.Windows(4, 4, 1, 1, 5), "f32"),
+    (24, 16, 1, 2, 128, A.Windows(8, 8, 4, 4, 100), "f32"),
 ]
 
 
 @pytest.mark.parametrize("H,W,B,Hh,d,spec,dt", SMALL)
 def test_small_ragged_full_compare(H, W, B, Hh, d, spec, dt):
     stale = isinstance(spec, A.Strips)
-    inp = WL.attention_inputs(B, Hh, d, H, W, seed=7 + H + W + d, dtype=dt, stale=stale)
+    inp = WL.attention_inputs(B, Hh, d, H, W, seed=7 + H + W + d, dtype=dt, stale=stale,
+                              text_tokens=A.text_tokens(spec))
     got = _run(inp, H, W, spec, dt)
     ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec)
     err = np.abs(got - ref).max()
@@ -83,7 +91,7 @@ def test_explicit_scale_and_halo_beyond_map():
 def _workload_spec(w):
     if w["mode"] == "strips":
         return A.Strips(w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
-    return A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"])
+    return A.Windows(w["tile_h"], w["tile_w"], w["halo_h"], w["halo_w"], w.get("text_tokens", 0))
 
 
 def _sample_queries(w, spec):
@@ -98,7 +106,11 @@ def _sample_queries(w, spec):
     tx = W // spec.tile_w
     ty = H // spec.tile_h
     pick = [0, tx // 2, (ty // 2) * tx + tx // 2, ty * tx - 1]
-    return np.concatenate([tiles[i][0] for i in sorted(set(pick))])
+    sample = [tiles[i][0] for i in sorted(set(pick))]
+    T = A.text_tokens(spec)
+    if T:  # the first, a middle and the last text queries
+        sample.append(np.array(sorted({0, 1, T // 2, T - 2, T - 1})))
+    return np.concatenate(sample)
 
 
 @pytest.mark.parametrize("name", list(WL.ATTENTION_WORKLOADS))
@@ -279,5 +291,57 @@ def test_late_large_logits_take_the_robust_pass(spec, H, W, d):
     inp = dict(q=q, k=k, v=v, k_stale=k.copy(), v_stale=v.copy())
     got = _run(inp, H, W, spec, "bf16")
     ref = A.attention_tier1(q, k, v, inp["k_stale"], inp["v_stale"], H, W, spec)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("spec", [A.Windows(2, 2, 1, 1, 3), A.Windows(4, 2, 0, 1, 9)])
+def test_joint_one_hot_values_expose_probability_rows(spec, dt):
+    """4x4 map after T text tokens, d = 64: V = one-hot over the T + 16 stored
+    tokens, so out[:, :T+16] is each query's probability row; it must be zero
+    off the query's key set (text + window for map queries, all for text)."""
+    H = W = 4
+    T = A.text_tokens(spec)
+    N = T + H * W
+    rng = np.random.Generator(np.random.PCG64(5))
+    q = rng.standard_normal((1, N, 1, 64), dtype=np.float32)
+    k = rng.standard_normal((1, N, 1, 64), dtype=np.float32)
+    if dt == "bf16":
+        q, k = WL.round_to_bf16(q), WL.round_to_bf16(k)
+    v = np.zeros((1, N, 1, 64), np.float32)
+    v[0, :, 0, :N] = np.eye(N)
+    got = _run(dict(q=q, k=k, v=v), H, W, spec, dt)[0, :, 0, :]
+    P = got[:, :N]
+    ref = A.attention_tier1(q, k, v, None, None, H, W, spec)[0, :, 0, :N]
+    sets = A.attended_sets(H, W, spec)
+    for t in range(N):
+        allowed = np.zeros(N, dtype=bool)
+        allowed[sets[t][0]] = True
+        assert np.all(P[t, ~allowed] == 0.0), f"query {t} weighs keys outside its set"
+        assert np.all(P[t, allowed] > 0.0), f"query {t} misses keys of its set"
+    tol = 1e-2 if dt == "bf16" else 1e-5
+    np.testing.assert_allclose(P.sum(1), 1.0, atol=tol)
+    np.testing.assert_allclose(P, ref, atol=tol)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_joint_text_logits_take_the_robust_pass(d):
+    """Text keys (read after each map tile's window) score ~100 log2 units above
+    the window's first keys: the fixed-shift pass overflows and the tile is redone
+    with its true row max."""
+    H = W = 16
+    T = 40
+    N = T + H * W
+    spec = A.Windows(8, 8, 4, 4, T)
+    rng = np.random.Generator(np.random.PCG64(22))
+    q = 0.05 * rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    k = 0.05 * rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    v = rng.standard_normal((1, N, 2, d), dtype=np.float32)
+    q[0, :, 0, 0] = 24.0
+    k[0, T - 3:T, 0, 0] = 24.0   # the last text keys align with every query
+    q, k, v = (WL.round_to_bf16(a) for a in (q, k, v))
+    got = _run(dict(q=q, k=k, v=v), H, W, spec, "bf16")
+    ref = A.attention_tier1(q, k, v, None, None, H, W, spec)
     assert np.isfinite(got).all()
     assert np.abs(got - ref).max() <= 2e-2
