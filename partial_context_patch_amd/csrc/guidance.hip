@@ -4,12 +4,12 @@
 // guidance of "ScaleDiff ..." (atlas.scime.ai), "Approach", written as one
 // filter of the difference (the filter is linear, so this equals
 // G*ref - G*x).  Separable Gaussian, reflect-101 borders.  Each workgroup
-// produces a 32x64 output tile: the tile plus an R-pixel apron of (ref - x)
-// is staged in LDS, filtered along rows into a second LDS buffer, then along
+// produces one output tile: the tile plus an R-pixel apron of (ref - x) is
+// staged in LDS, filtered along rows into a second LDS buffer, then along
 // columns straight into the output.  Bandwidth-bound: x and ref are read once
 // from HBM (the apron re-reads hit L2), out is written once: 12 bytes of HBM
-// traffic per element.  sg_blend_fixed is the radius-12 (sigma = 4) form;
-// sg_blend_kernel serves any other radius.
+// traffic per element.  sg_blend_tile<12, ...> is the radius-12 (sigma = 4)
+// form; sg_blend_kernel serves any other radius.
 //
 // asg_blend: out = eps + w * mask * (eps_ref_prev - eps), element-wise
 // (asynchronous structure guidance, pith.science verdict on ASGDiffusion,
@@ -70,29 +70,31 @@ __global__ __launch_bounds__(kThreads) void sg_blend_kernel(const SgArgs a) {
 }
 
 
-// Radius known at compile time (sigma = 4 -> R = 12): 64 x 32 output tile,
-// every thread produces 8 outputs per pass from a register window of 8 + 2R
-// inputs, so each staged value is read from LDS about (8 + 2R) / 8 times
-// instead of 2R + 1 times, and no index needs a run-time division.
-template <int R>
-__global__ __launch_bounds__(kThreads) void sg_blend_fixed(const SgArgs a) {
-  constexpr int LW = kTW + 2 * R, LH = kTH + 2 * R, WIN = 8 + 2 * R;
+// Radius known at compile time (sigma = 4 -> R = 12): a TW x TH output tile per
+// workgroup of NTH threads.  The row pass gives each thread RO outputs from a
+// register window of RO + 2R inputs, the column pass CO outputs from CO + 2R,
+// so each staged value is read from LDS about (RO + 2R) / RO times instead of
+// 2R + 1 times, and no index needs a run-time division by the tile width.
+// Tiles whose apron lies inside the image stage 16-byte vectors; the others
+// reflect (101) index by index.  The launch is one round of large workgroups
+// (64 x 64 tiles, 1024 threads: one per CU at 4 x 512 x 512): bigger tiles
+// re-read less apron, and sixteen waves per CU hide the load latency.
+template <int R, int TW, int TH, int RO, int CO, int NTH>
+__global__ __launch_bounds__(NTH) void sg_blend_tile(const SgArgs a) {
+  constexpr int kThreads = NTH;
+  constexpr int LW = TW + 2 * R, LH = TH + 2 * R;
   __shared__ __attribute__((aligned(16))) float diff[LH * LW];
-  __shared__ float tmp[LH * kTW];
-  __shared__ __attribute__((aligned(16))) float xs[kTH * kTW];  // x over the output tile itself
-  const int r0 = blockIdx.y * kTH, c0 = blockIdx.x * kTW;
+  __shared__ float tmp[LH * TW];
+  __shared__ __attribute__((aligned(16))) float xs[TH * TW];
+  const int r0 = blockIdx.y * TH, c0 = blockIdx.x * TW;
   const size_t pb = (size_t)blockIdx.z * a.H * a.W;
   const float* x = a.x + pb;
   const float* ref = a.ref + pb;
   float taps[2 * R + 1];
 #pragma unroll
   for (int t = 0; t <= 2 * R; ++t) taps[t] = a.taps[t];
-
-  // stage ref - x over the tile and its apron.  Tiles whose apron lies inside
-  // the image read 16-byte vectors; the others reflect (101) index by index.
-  // Fixed, unrolled trip counts let every load of a thread be in flight at once.
-  static_assert(LW % 4 == 0 && R % 4 == 0 && kTW % 4 == 0, "vector staging");
-  const bool inside = r0 - R >= 0 && c0 - R >= 0 && r0 + kTH + R <= a.H && c0 + kTW + R <= a.W && (a.W & 3) == 0;
+  static_assert(LW % 4 == 0 && R % 4 == 0 && TW % 4 == 0, "vector staging");
+  const bool inside = r0 - R >= 0 && c0 - R >= 0 && r0 + TH + R <= a.H && c0 + TW + R <= a.W && (a.W & 3) == 0;
   if (inside) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int LW4 = LW / 4;
@@ -116,67 +118,67 @@ __global__ __launch_bounds__(kThreads) void sg_blend_fixed(const SgArgs a) {
       if (i < LH * LW4) {
         *(f32x4*)&diff[4 * i] = rv[k] - xv[k];
         const int rr = i / LW4 - R, cc = 4 * (i % LW4) - R;
-        if (rr >= 0 && rr < kTH && cc >= 0 && cc < kTW) *(f32x4*)&xs[rr * kTW + cc] = xv[k];
+        if (rr >= 0 && rr < TH && cc >= 0 && cc < TW) *(f32x4*)&xs[rr * TW + cc] = xv[k];
       }
     }
   } else {
-  constexpr int kStage = (LH * LW + kThreads - 1) / kThreads;
-  float rv[kStage], xv[kStage];
+    constexpr int kStage = (LH * LW + kThreads - 1) / kThreads;
+    float rv[kStage], xv[kStage];
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    const int rr = i / LW, cc = i - rr * LW;
-    int gr = r0 - R + rr, gc = c0 - R + cc;
-    if ((unsigned)gr >= (unsigned)a.H) gr = reflect101(gr, a.H);
-    if ((unsigned)gc >= (unsigned)a.W) gc = reflect101(gc, a.W);
-    const size_t at = (size_t)gr * a.W + gc;
-    rv[k] = 0.0f;
-    xv[k] = 0.0f;
-    if (i < LH * LW) {
-      rv[k] = ref[at];
-      xv[k] = x[at];
+    for (int k = 0; k < kStage; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      const int rr = i / LW, cc = i - rr * LW;
+      int gr = r0 - R + rr, gc = c0 - R + cc;
+      if ((unsigned)gr >= (unsigned)a.H) gr = reflect101(gr, a.H);
+      if ((unsigned)gc >= (unsigned)a.W) gc = reflect101(gc, a.W);
+      const size_t at = (size_t)gr * a.W + gc;
+      rv[k] = 0.0f;
+      xv[k] = 0.0f;
+      if (i < LH * LW) {
+        rv[k] = ref[at];
+        xv[k] = x[at];
+      }
     }
-  }
 #pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    if (i < LH * LW) {
-      diff[i] = rv[k] - xv[k];
-      const int rr = i / LW - R, cc = i % LW - R;
-      if (rr >= 0 && rr < kTH && cc >= 0 && cc < kTW) xs[rr * kTW + cc] = xv[k];
+    for (int k = 0; k < kStage; ++k) {
+      const int i = threadIdx.x + k * kThreads;
+      if (i < LH * LW) {
+        diff[i] = rv[k] - xv[k];
+        const int rr = i / LW - R, cc = i % LW - R;
+        if (rr >= 0 && rr < TH && cc >= 0 && cc < TW) xs[rr * TW + cc] = xv[k];
+      }
     }
-  }
   }
   __syncthreads();
-  // rows: thread -> (row, 8-column segment); LH rows x 8 segments
-  for (int job = threadIdx.x; job < LH * (kTW / 8); job += kThreads) {
-    const int rr = job >> 3, cs = (job & 7) * 8;
-    float w[WIN];
+  constexpr int RSEG = TW / RO, RWIN = RO + 2 * R;
+  for (int job = threadIdx.x; job < LH * RSEG; job += kThreads) {
+    const int rr = job / RSEG, cs = (job % RSEG) * RO;
+    float w[RWIN];
 #pragma unroll
-    for (int k = 0; k < WIN; ++k) w[k] = diff[rr * LW + cs + k];
+    for (int k = 0; k < RWIN; ++k) w[k] = diff[rr * LW + cs + k];
 #pragma unroll
-    for (int o = 0; o < 8; ++o) {
+    for (int o = 0; o < RO; ++o) {
       float acc = 0.0f;
 #pragma unroll
       for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(taps[t], w[o + t], acc);
-      tmp[rr * kTW + cs + o] = acc;
+      tmp[rr * TW + cs + o] = acc;
     }
   }
   __syncthreads();
-  // columns: thread -> (column, 8-row segment); 64 columns x 4 segments
-  {
-    const int cc = threadIdx.x & (kTW - 1), rs = (threadIdx.x >> 6) * 8;
-    float w[WIN];
+  constexpr int CSEG = TH / CO, CWIN = CO + 2 * R;
+  for (int job = threadIdx.x; job < TW * CSEG; job += kThreads) {
+    const int cc = job % TW, rs = (job / TW) * CO;
+    float w[CWIN];
 #pragma unroll
-    for (int k = 0; k < WIN; ++k) w[k] = tmp[(rs + k) * kTW + cc];
+    for (int k = 0; k < CWIN; ++k) w[k] = tmp[(rs + k) * TW + cc];
     const int gc = c0 + cc;
 #pragma unroll
-    for (int o = 0; o < 8; ++o) {
+    for (int o = 0; o < CO; ++o) {
       const int gr = r0 + rs + o;
       float acc = 0.0f;
 #pragma unroll
       for (int t = 0; t <= 2 * R; ++t) acc = __builtin_fmaf(taps[t], w[o + t], acc);
-      if (gr < a.H && gc < a.W) a.out[pb + (size_t)gr * a.W + gc] = __builtin_fmaf(a.w, acc, xs[(rs + o) * kTW + cc]);
+      if (gr < a.H && gc < a.W) a.out[pb + (size_t)gr * a.W + gc] = __builtin_fmaf(a.w, acc, xs[(rs + o) * TW + cc]);
     }
   }
 }
@@ -207,12 +209,13 @@ __global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st) {
-  const dim3 grid((a.W + kTW - 1) / kTW, (a.H + kTH - 1) / kTH, a.planes), block(kThreads);
-  static_assert(kTH == 32 && kTW == 64 && kThreads == 256, "sg_blend_fixed thread mapping");
   if (a.R == 12) {
-    hipLaunchKernelGGL((sg_blend_fixed<12>), grid, block, 0, st, a);
+    constexpr int TW = 64, TH = 64, NTH = 1024;
+    const dim3 grid((a.W + TW - 1) / TW, (a.H + TH - 1) / TH, a.planes);
+    hipLaunchKernelGGL((sg_blend_tile<12, TW, TH, 8, 4, NTH>), grid, dim3(NTH), 0, st, a);
     return hipGetLastError();
   }
+  const dim3 grid((a.W + kTW - 1) / kTW, (a.H + kTH - 1) / kTH, a.planes), block(kThreads);
   const size_t lds = sizeof(float) * ((size_t)(kTH + 2 * a.R) * (kTW + 2 * a.R) + (size_t)(kTH + 2 * a.R) * kTW);
   hipLaunchKernelGGL(sg_blend_kernel, grid, block, lds, st, a);
   return hipGetLastError();
