@@ -432,39 +432,41 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
   // row max of the tile).
   //
   // Each 64-key block is one straight-line body, specialised at compile time
-  // for the first block (FIRST: scores unshifted, the max is taken) and for
-  // blocks that end inside the padding (MASK): the score MFMAs of both 32-key
-  // halves are issued before the first half's exp work, so the second half's
-  // MFMAs run while the VALU does the first half's softmax.
-  auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn, auto first_tag,
-                   auto mask_tag) __attribute__((always_inline)) {
+  // for the first block (FIRST: scores unshifted, the max is taken): the score
+  // MFMAs of both 32-key halves are issued before the first half's exp work,
+  // so the second half's MFMAs run while the VALU does the first half's
+  // softmax.  Blocks that end inside a run's padding take the same body.
+  auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn,
+                   auto first_tag) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
-    constexpr bool MASK = decltype(mask_tag)::value;
     // this wave's copies into tile kb are done; after the barrier, everyone's are
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int valid = MASK ? cur_left : kBN;  // the cursor is on block kb
+    const int valid = cur_left;  // the cursor is on block kb
+    // a block that ends inside its run's padding (at most one per run)
+    const bool part = PARTIAL && valid < kBN;
     if (kb + 1 < nkb) {
       cursor_next();
       fetch(skn, svn);
     }
 
-    // S^T of half mt (exp2 domain; shifted by -m unless FIRST)
+    // S^T of half mt in the exp2 domain, shifted by the C operand (FIRST:
+    // the shift is zero, so these are the raw scores)
     auto scores = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int row = mt * 32 + krow;
         const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          sc[nt] = mfma(kf, qf[nt][ks], ks == 0 ? (FIRST ? f32x16{} : shift[nt]) : sc[nt]);
+        for (int nt = 0; nt < NT; ++nt) sc[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : sc[nt]);
       }
     };
-    // keys past the end of their run: entry j of lane half g is key 8g + j
-    // (j < 8) or 8g + j + 8 (j >= 8) of the half
+    // Keys past the end of their run: entry j of lane half g is key 8g + j
+    // (j < 8) or 8g + j + 8 (j >= 8) of half mt; their scores become -inf.
+    // Only blocks that end inside a run's padding take this step, between the
+    // scheduled regions, so full blocks and partial ones share one body.
     auto mask = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
-      if (!MASK) return;
       const int t = valid - mt * 32 - 8 * g;
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -500,22 +502,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
 
     f32x16 s0[NT], s1[NT];
     bf16x8 pa0[NT], pa1[NT], pb0[NT], pb1[NT];
-    if (MASK && !FIRST) {
-      // a block that ends inside the padding (at most one per key run): the
-      // halves one after the other, which keeps only one score tile live
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        __builtin_amdgcn_sched_barrier(0);
-        scores(mt, s0);
-        mask(mt, s0);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[nt], pa0[nt], pa1[nt], l[nt]);
-        pv(mt, pa0, pa1);
-      }
-      return;
-    }
     scores(0, s0);
-    mask(0, s0);
+    if (part) mask(0, s0);
     if (FIRST) {
       // the exact row max of the first 32 keys becomes the shift; half 1 then
       // takes the ordinary path with the shift inside its MFMA
@@ -528,15 +516,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
       }
       pv(0, pa0, pa1);
       __builtin_amdgcn_sched_barrier(0);
-      // (scores() reads FIRST, so half 1 is written out with the shift here)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int row = 32 + krow;
-        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s1[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : s1[nt]);
-      }
-      mask(1, s1);
+      scores(1, s1);
+      if (part) mask(1, s1);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
       pv(1, pb0, pb1);
@@ -554,7 +535,7 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
       __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);   // VALU
     }
     __builtin_amdgcn_sched_barrier(0);
-    mask(1, s1);
+    if (part) mask(1, s1);
     __builtin_amdgcn_sched_barrier(0);
     // half 0's PV MFMAs run while the VALU does half 1's weights
     pv(0, pa0, pa1);
@@ -569,13 +550,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
     __builtin_amdgcn_sched_barrier(0);
     pv(1, pb0, pb1);
   };
-  // block kb of the pass, picking the body for partial blocks at run time
-  auto any_block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn) __attribute__((always_inline)) {
-    if (PARTIAL && cur_left < kBN)
-      block(kb, skb, svb, skn, svn, std::false_type{}, std::integral_constant<bool, PARTIAL>{});
-    else
-      block(kb, skb, svb, skn, svn, std::false_type{}, std::false_type{});
-  };
   auto pass = [&](bool preset) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -586,14 +560,12 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
     cursor_reset();
     fetch(sk0, sv0);
     if (preset)
-      any_block(0, sk0, sv0, sk1, sv1);
-    else if (PARTIAL && cur_left < kBN)
-      block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::integral_constant<bool, PARTIAL>{});
+      block(0, sk0, sv0, sk1, sv1, std::false_type{});
     else
-      block(0, sk0, sv0, sk1, sv1, std::true_type{}, std::false_type{});
+      block(0, sk0, sv0, sk1, sv1, std::true_type{});
     for (int kb = 1; kb < nkb; kb += 2) {
-      any_block(kb, sk1, sv1, sk0, sv0);
-      if (kb + 1 < nkb) any_block(kb + 1, sk0, sv0, sk1, sv1);
+      block(kb, sk1, sv1, sk0, sv0, std::false_type{});
+      if (kb + 1 < nkb) block(kb + 1, sk0, sv0, sk1, sv1, std::false_type{});
     }
   };
 
