@@ -16,6 +16,10 @@ The JSON line carries:
                steps, frac_at_sclk the fraction of the peak at that clock;
   cpu_baseline -- the fp64 oracle timed on a bounded sample of the same
                workload on this host's cores (rank 0, N=1 only).
+  roofline.measured_mfma_ceiling -- after the timed steps, a dense
+               v_mfma_f32_32x32x16_bf16 stream on random and on constant
+               operands: what this GPU sustains under its clock and power
+               management (the published peak assumes 2.4 GHz throughout).
 """
 from __future__ import annotations
 
@@ -76,6 +80,26 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
     }
 
 
+def mfma_ceiling():
+    """Run the dense-MFMA calibration program (a child process; about 3 s) and
+    return its measurements, or None when it is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "partial_context_patch_amd", "calib", "mfma_ceiling")
+    if not os.path.exists(exe):
+        log("mfma ceiling: calibration program not built")
+        return None
+    log("measuring the dense bf16 MFMA ceiling (random and constant operands)")
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        log("mfma ceiling: timed out")
+        return None
+    if r.returncode != 0:
+        log(f"mfma ceiling: failed ({r.stderr.strip()[-200:]})")
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +111,9 @@ def main() -> int:
                     help="seconds of back-to-back steps before the warm-up steps, so that the GPU's clock "
                          "governor has raised the shader clock to its sustained level (it ramps over ~1-2 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the dense-MFMA calibration run (after the timed steps) that measures the "
+                         "bf16 MFMA throughput this GPU sustains on random and on constant operands")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (outside the timed region) so that a "
                          "counter profile of this command can scale its byte counters")
@@ -182,6 +209,10 @@ def main() -> int:
     traffic = profiling.load_traffic(name)
     sclk = clock.get("sclk_mhz")
 
+    ceiling = None
+    if not args.no_mfma_ceiling:
+        ceiling = mfma_ceiling()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample of the same workload")
@@ -216,7 +247,10 @@ def main() -> int:
                      "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg, 5),
                      "sclk_mhz": sclk, "sclk_samples": clock["sclk_samples"],
                      "power_w": clock["power_w"], "power_cap_w": clock["power_cap_w"],
-                     "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4)},
+                     "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4),
+                     "measured_mfma_ceiling": ceiling,
+                     "frac_of_measured_ceiling": (round(achieved / ceiling["random_tflops"], 4)
+                                                  if ceiling and ceiling.get("random_tflops") else None)},
         "sg_blend": {"bound": "hbm", "achieved": round(sg_bytes / (sg_avg * 1e-3) / 1e9, 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(sg_bytes / (sg_avg * 1e-3) / 1e9 / 8000.0, 4),
                      "algorithmic_bytes": sg_bytes, "avg_launch_ms": round(sg_avg, 5)},
