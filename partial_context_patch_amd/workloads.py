@@ -63,6 +63,12 @@ ATTENTION_WORKLOADS: Dict[str, dict] = {
         rms_qk=True,
         what="FLUX 4096^2 DiT, NPA: 256x256 packed tokens, 24x128 heads, 32x32 query tiles, 64x64 windows",
     ),
+    # Strips at head_dim 128 (a DiT run with PCPP): parity case.
+    "flux2048_strips": dict(
+        mode="strips", batch=1, heads=24, head_dim=128, map_h=64, map_w=64,
+        num_strips=4, p=0.3, dtype="bf16", seed=1010, rms_qk=True,
+        what="FLUX-shaped 2048^2 (64x64 packed tokens), 24x128 heads, 4 strips, p=0.3",
+    ),
     # FLUX's joint attention with the prompt's text tokens stored before the
     # map's tokens (global: map queries also see every text token, text queries
     # see everything).
