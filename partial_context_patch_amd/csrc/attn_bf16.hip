@@ -493,13 +493,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
       }
     };
 
-    // Instruction counts of the phases, for the interleave patterns below.
-    constexpr int kSMfma = KS * NT;        // MFMAs of one half's S^T
-    constexpr int kSReads = KS;            // its K-fragment reads
-    constexpr int kPVMfma = DT * 2 * NT;   // MFMAs of one half's PV
-    constexpr int kPVReads = DT * 4;       // its V^T transpose reads
-    constexpr int kExpValu = NT * 33;      // exp, pack, row-sum VALU of one half
-
     f32x16 s0[NT], s1[NT];
     bf16x8 pa0[NT], pa1[NT], pb0[NT], pb1[NT];
     scores(0, s0);
@@ -524,29 +517,18 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
       return;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // half 1's score MFMAs run while the VALU turns half 0's scores into weights
+    // half 1's score MFMAs run while the VALU turns half 0's scores into
+    // weights (one region: the compiler interleaves them)
     scores(1, s1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[nt], pa0[nt], pa1[nt], l[nt]);
-#pragma unroll
-    for (int i = 0; i < kSMfma; ++i) {
-      if (i < kSReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);   // VALU
-    }
     __builtin_amdgcn_sched_barrier(0);
     if (part) mask(1, s1);
     __builtin_amdgcn_sched_barrier(0);
-    // half 0's PV MFMAs run while the VALU does half 1's weights
+    // half 0's PV MFMAs run while the VALU does half 1's weights (one region)
     pv(0, pa0, pa1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
-#pragma unroll
-    for (int i = 0; i < kPVMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kPVReads / kPVMfma, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kPVMfma, 0);  // VALU
-    }
     __builtin_amdgcn_sched_barrier(0);
     pv(1, pb0, pb1);
   };
