@@ -229,7 +229,6 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
 
   const TileRuns tr = tile_runs(a.g, tile);
   const int nq = tr.q.count();
-  const int nk = tr.nk[0] + tr.nk[1] + tr.nk[2];
   const int64_t bh = (int64_t)b * a.sb + (int64_t)head * a.sh;
   const float inv_qlen = 1.0f / (float)tr.q.row_len;
   const float inv_klen = 1.0f / (float)tr.k[0].row_len;
