@@ -35,6 +35,18 @@ if ROOT not in sys.path:
 
 # Dense bf16 MFMA peak of MI355X: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
 PEAK_BF16_TFLOPS = 2516.6
+# fp32 vector peak of MI355X (the fp32 kernel runs on the vector ALUs).
+PEAK_F32_VECTOR_TFLOPS = 157.3
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def log(msg: str) -> None:
@@ -76,7 +88,7 @@ def cpu_baseline(name: str, inp: dict, budget_s: float) -> dict:
         "kind": "oracle",
         "sample": f"{n_tiles} (batch, head, query tile) units of {len(tiles) * len(heads)} "
                   f"({done_pairs} attended pairs, {4 * d * done_pairs / 1e9:.1f} useful GFLOP) in {secs:.1f} s; "
-                  f"fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}",
+                  f"fp64 numpy, BLAS threads={threads}, host cpus={os.cpu_count()}, cpu: {cpu_model()}",
     }
 
 
@@ -199,9 +211,10 @@ def main() -> int:
     attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
     sg_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_avg = float(np.mean(attn_ms))
+    attn_p10, attn_med, attn_p90 = (float(v) for v in np.percentile(attn_ms, [10, 50, 90]))
     sg_avg = float(np.mean(sg_ms))
     log(f"step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms); attention avg {attn_avg:.4f} ms "
-        f"median {float(np.median(attn_ms)):.4f} min {min(attn_ms):.4f} max {max(attn_ms):.4f}")
+        f"p10 {attn_p10:.4f} median {attn_med:.4f} p90 {attn_p90:.4f} min {min(attn_ms):.4f} max {max(attn_ms):.4f}")
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_avg * 1e-3) / 1e12
     # structure-guidance blend: reads x and ref, writes out, 4 bytes each per element
@@ -221,10 +234,14 @@ def main() -> int:
     cfg = {"workload": name, "what": w["what"], "batch": w["batch"], "heads": w["heads"],
            "head_dim": w["head_dim"], "map": f"{w['map_h']}x{w['map_w']}",
            "useful_gflop_per_step": flops / 1e9, "sg_blend": sgw["what"]}
+    bf16 = w["dtype"] == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VECTOR_TFLOPS
     if w["mode"] == "strips":
         cfg.update(strips=w["num_strips"], p=w.get("p"), halo_rows=w.get("halo_rows"))
     else:
         cfg.update(tile=f"{w['tile_h']}x{w['tile_w']}", halo=w["halo_h"])
+        if w.get("text_tokens"):
+            cfg.update(text_tokens=w["text_tokens"])
     rec = {
         "metric": "useful partial-attention TFLOP/s & % of bf16 MFMA peak per denoise step",
         "value": round(value, 2),
@@ -241,16 +258,17 @@ def main() -> int:
         "dtype": w["dtype"],
         "data": "synthetic (seeded N(0,1) activations of the workload's shape; no weights or datasets)",
         "config": cfg,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "kernel": "attn_bf16_kernel", "avg_launch_ms": round(attn_avg, 5),
+        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None if (traffic is None or not bf16) else int(traffic),
+                     "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel", "avg_launch_ms": round(attn_avg, 5),
+                     "launch_ms_p10_median_p90": [round(attn_p10, 5), round(attn_med, 5), round(attn_p90, 5)],
                      "sclk_mhz": sclk, "sclk_samples": clock["sclk_samples"],
                      "power_w": clock["power_w"], "power_cap_w": clock["power_cap_w"],
-                     "frac_at_sclk": None if not sclk else round(achieved / (PEAK_BF16_TFLOPS * sclk / 2400.0), 4),
+                     "frac_at_sclk": None if not sclk else round(achieved / (peak * sclk / 2400.0), 4),
                      "measured_mfma_ceiling": ceiling,
                      "frac_of_measured_ceiling": (round(achieved / ceiling["random_tflops"], 4)
-                                                  if ceiling and ceiling.get("random_tflops") else None)},
+                                                  if bf16 and ceiling and ceiling.get("random_tflops") else None)},
         "sg_blend": {"bound": "hbm", "achieved": round(sg_bytes / (sg_avg * 1e-3) / 1e9, 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(sg_bytes / (sg_avg * 1e-3) / 1e9 / 8000.0, 4),
                      "algorithmic_bytes": sg_bytes, "avg_launch_ms": round(sg_avg, 5)},
