@@ -115,10 +115,16 @@ struct AttnArgs {
 // The text tile's workgroups come first: each one walks every stored token,
 // many times the keys of a map tile, so they are started first (spread over
 // the XCDs by the hardware's round-robin) rather than left as a tail.  The map
-// tiles' workgroups follow; with `remap`, hardware ids are regrouped so that
-// each XCD runs one contiguous range of them (the query blocks of a tile, and
-// neighbouring tiles, share K/V through that XCD's L2).  Blocks are dealt to
-// the 8 XCDs round-robin, so the remap keeps each id's class mod 8.
+// tiles follow as units of (tile, batch, head), each unit's query blocks
+// consecutive.  Workgroups are dealt to the 8 XCDs round-robin by id; with
+// `remap` the ids are regrouped so that all query blocks of a unit run on one
+// XCD (they share the unit's K/V through that XCD's L2):
+//   windows: each XCD runs one contiguous range of units, so neighbouring
+//            tiles of a head (whose windows overlap) share that L2 too;
+//   strips:  units are listed interior strips first, border strips (one
+//            stale halo, fewer keys) last, and dealt round-robin over the
+//            XCDs; each XCD then runs its longest units first, which keeps the
+//            end of the launch even.
 struct BlockCoord {
   int32_t qb, tile, head, b;
 };
@@ -129,20 +135,43 @@ NPA_HD int32_t xcd_remap(int32_t i, int32_t n) {
   return (x < rem) ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
 }
 
+// Strip of rank r with the border strips (0 and n-1) listed last; a
+// bijection on 0 .. n-1.
+NPA_HD int32_t border_last(int32_t r, int32_t n) {
+  return n < 3 ? r : (r < n - 2 ? r + 1 : (r == n - 2 ? 0 : n - 1));
+}
+
 NPA_HD BlockCoord decode_block(const AttnArgs& a, int32_t i, bool remap) {
   BlockCoord c;
   int32_t rest;
+  const int32_t j = i - a.text_blocks;
   if (i < a.text_blocks) {
     c.qb = i % a.text_qblocks;
     rest = i / a.text_qblocks;
     c.tile = a.g.n_img;
-  } else {
-    int32_t j = i - a.text_blocks;
-    if (remap) j = xcd_remap(j, a.nblocks - a.text_blocks);
-    c.qb = j % a.qblocks;
-    rest = j / a.qblocks;
+  } else if (!remap || a.g.mode != NPA_MODE_STRIPS) {
+    const int32_t jj = remap ? xcd_remap(j, a.nblocks - a.text_blocks) : j;
+    c.qb = jj % a.qblocks;
+    rest = jj / a.qblocks;
     c.tile = rest % a.g.n_img;
     rest /= a.g.n_img;
+  } else {
+    // units (rank, batch * heads + head), rank slowest; the first 8*floor(U/8)
+    // units are dealt round-robin over the XCDs, the rest (the smallest) in order
+    const int32_t units = (a.nblocks - a.text_blocks) / a.qblocks;
+    const int32_t dealt = (units & ~7) * a.qblocks;
+    int32_t unit;
+    if (j < dealt) {
+      const int32_t k = j >> 3;
+      unit = (k / a.qblocks) * 8 + (j & 7);
+      c.qb = k % a.qblocks;
+    } else {
+      unit = (units & ~7) + (j - dealt) / a.qblocks;
+      c.qb = (j - dealt) % a.qblocks;
+    }
+    const int32_t bh = a.B * a.Hh;
+    c.tile = border_last(unit / bh, a.g.n_img);
+    rest = unit % bh;
   }
   c.head = rest % a.Hh;
   c.b = rest / a.Hh;
