@@ -131,8 +131,9 @@ def main() -> int:
                          "counter profile of this command can scale its byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the partial-attention path is built and timed on a single MI355X; "
-              "runs on more than one GPU are not part of this build (see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU: the partial-attention kernels run and are timed on a single MI355X; "
+              "multi-GPU runs are not supported (the path would shard by (batch, head, tile) units, or by strips "
+              "with a stale-halo exchange between neighbouring GPUs).",
               file=sys.stderr)
         return 2
 
