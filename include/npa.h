@@ -151,9 +151,8 @@ npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t 
                           int32_t c, int32_t h, int32_t w, float w_t, float sigma,
                           void* hip_stream);
 
-/* Asynchronous structure-guidance correction: "Training-free diffusion
- * generates high-res images in parallel with stale guidance" (pith.science
- * verdict on ASGDiffusion, "core_discovery"):
+/* Asynchronous structure-guidance correction: the pith.science verdict page
+ * on ASGDiffusion (arXiv 2412.06163), section "core_discovery":
  *   out = eps + w_t * mask * (eps_ref_prev - eps)        element-wise,
  * where eps_ref_prev is the reference patch's prediction from the previous
  * step and mask the normalised cross-attention mask (caller-supplied).

@@ -17,9 +17,9 @@ where the page is silent:
 * the latent is [C, H, W] (a leading batch dimension is allowed); w_t is a
   scalar supplied by the caller -- its schedule is not part of the blend.
 
-The asynchronous-guidance blend of "Training-free diffusion generates high-res
-images in parallel with stale guidance" (pith.science verdict on ASGDiffusion,
-"core_discovery" / "key_machinery") is the element-wise form
+The asynchronous-guidance blend of ASGDiffusion (the pith.science verdict page
+on arXiv 2412.06163, sections "core_discovery" and "key_machinery") is the
+element-wise form
 
     eps_corrected = eps + w_t * M * (eps_ref_prev - eps)
 
