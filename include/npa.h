@@ -72,7 +72,9 @@ typedef enum { NPA_MODE_STRIPS = 0, NPA_MODE_WINDOW = 1 } npa_mode_t;
  * text_tokens, when there are any: t = text_tokens + r*map_w + c).  Every
  * pointer must be 16-byte aligned and stride_b/stride_n/stride_h must keep
  * each head's row 16-byte aligned.  Limits: text_tokens + map_h*map_w <= 2^24,
- * batch*heads*tiles*blocks < 2^31. */
+ * batch*heads*tiles*blocks < 2^31.  batch and heads may be 0: such a call is
+ * validated, computes nothing, touches no memory and returns NPA_OK (its
+ * pointers may then be NULL); head_dim, map_h, map_w are >= 1. */
 typedef struct {
   int32_t batch, heads, head_dim; /* head_dim: 64 or 128 for bf16; 32/64/128 for f32 */
   int32_t map_h, map_w;
@@ -145,7 +147,8 @@ int64_t npa_useful_flops(const npa_layout_t* layout, const npa_halo_t* halo);
  * exp(-k^2/(2 sigma^2)) normalised to 1, reflect-101 borders.
  * x, ref, out: fp32 device tensors [n, c, h, w] contiguous, 16-byte aligned;
  * out must not alias x or ref (the stencil reads neighbours).  sigma in
- * (0, 8]; h, w >= 1.  With w_t = 1 this is also latent frequency mixing:
+ * (0, 8]; h, w >= 1; n, c >= 0 (n*c = 0: nothing to do, NPA_OK, pointers
+ * unchecked).  With w_t = 1 this is also latent frequency mixing:
  * low frequencies of ref, high frequencies of x. */
 npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t n,
                           int32_t c, int32_t h, int32_t w, float w_t, float sigma,

@@ -45,8 +45,8 @@ int32_t halo_from_p(float p, int32_t s) {
 // Validate the layout and halo; build the plan parameters.
 npa_status_t make_geo(const npa_layout_t* L, const npa_halo_t* h, npa::Geo* g) {
   if (!L || !h) return fail(NPA_ERR_INVALID_ARG, "layout and halo must not be NULL");
-  if (L->batch < 1 || L->heads < 1 || L->head_dim < 1 || L->map_h < 1 || L->map_w < 1)
-    return fail(NPA_ERR_SHAPE, "batch, heads, head_dim, map_h, map_w must be >= 1");
+  if (L->batch < 0 || L->heads < 0 || L->head_dim < 1 || L->map_h < 1 || L->map_w < 1)
+    return fail(NPA_ERR_SHAPE, "batch and heads must be >= 0, head_dim, map_h and map_w >= 1");
   if (h->text_tokens < 0) return fail(NPA_ERR_SHAPE, "text_tokens=%d must be >= 0", h->text_tokens);
   if ((int64_t)h->text_tokens + (int64_t)L->map_h * L->map_w > (int64_t(1) << 24))
     return fail(NPA_ERR_SHAPE, "text_tokens + map_h*map_w = %lld exceeds 2^24 tokens",
@@ -193,6 +193,8 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   if (block_m == 0)
     return fail(NPA_ERR_UNSUPPORTED, "head_dim=%d is not supported for %s", L->head_dim,
                 L->dtype == NPA_BF16 ? "bf16 (64 or 128)" : "f32 (32, 64 or 128)");
+  // no (batch, head) slice: a valid call with nothing to compute or touch
+  if (L->batch == 0 || L->heads == 0) return ok();
   if (!Q || !K_fresh || !V_fresh || !out)
     return fail(NPA_ERR_INVALID_ARG, "Q, K_fresh, V_fresh and out must not be NULL");
   const bool stale = reads_stale(g);
@@ -257,12 +259,13 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
 
 npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t n, int32_t c,
                           int32_t h, int32_t w, float w_t, float sigma, void* hip_stream) {
+  if (n < 0 || c < 0 || h < 1 || w < 1) return fail(NPA_ERR_SHAPE, "n, c must be >= 0 and h, w >= 1");
+  if (!(sigma > 0.0f && sigma <= 8.0f)) return fail(NPA_ERR_SHAPE, "sigma=%g must lie in (0, 8]", (double)sigma);
+  if (!std::isfinite(w_t)) return fail(NPA_ERR_INVALID_ARG, "w_t must be finite");
+  if (n == 0 || c == 0) return ok();  // no plane: nothing to compute or touch
   if (!x || !ref || !out) return fail(NPA_ERR_INVALID_ARG, "x, ref and out must not be NULL");
   if (!aligned16(x) || !aligned16(ref) || !aligned16(out))
     return fail(NPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  if (n < 1 || c < 1 || h < 1 || w < 1) return fail(NPA_ERR_SHAPE, "n, c, h, w must be >= 1");
-  if (!(sigma > 0.0f && sigma <= 8.0f)) return fail(NPA_ERR_SHAPE, "sigma=%g must lie in (0, 8]", (double)sigma);
-  if (!std::isfinite(w_t)) return fail(NPA_ERR_INVALID_ARG, "w_t must be finite");
   const int64_t planes = (int64_t)n * c;
   if (planes > 65535) return fail(NPA_ERR_SHAPE, "n*c=%lld exceeds 65535 planes", (long long)planes);
   const uintptr_t bytes = (uintptr_t)planes * h * w * sizeof(float);

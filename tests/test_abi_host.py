@@ -148,9 +148,12 @@ def test_validation_errors(lib):
     assert _status(lib, good_L, npa.make_halo(strips=4, p=-0.1)) == npa.NPA_ERR_SHAPE
     assert _status(lib, good_L, npa.make_halo(tile=(5, 8), halo=(1, 1))) == npa.NPA_ERR_SHAPE
     assert _status(lib, good_L, npa.make_halo(tile=(8, 8), halo=(-1, 1))) == npa.NPA_ERR_SHAPE
-    zero = npa.make_layout(1, 2, 64, 32, 32)
-    zero.batch = 0
-    assert _status(lib, zero, strips) == npa.NPA_ERR_SHAPE
+    neg = npa.make_layout(1, 2, 64, 32, 32)
+    neg.batch = -1
+    assert _status(lib, neg, strips) == npa.NPA_ERR_SHAPE
+    neg = npa.make_layout(1, 2, 64, 32, 32)
+    neg.heads = -2
+    assert _status(lib, neg, strips) == npa.NPA_ERR_SHAPE
     huge = npa.make_layout(1, 1, 64, 8192, 4096)
     assert _status(lib, huge, npa.make_halo(tile=(64, 64), halo=(0, 0))) == npa.NPA_ERR_SHAPE
     # text tokens: window mode only, >= 0, within the token limit
@@ -183,6 +186,28 @@ def test_validation_errors(lib):
     assert lib.npa_sg_blend(0, 2 << 20, 3 << 20, 1, 4, 8, 8, 0.5, 4.0, None) == npa.NPA_ERR_INVALID_ARG
     assert lib.npa_asg_blend(1 << 20, 2 << 20, 3 << 20, 4 << 20, -1, 0.5, None) == npa.NPA_ERR_SHAPE
     assert lib.npa_asg_blend(1 << 20, 2 << 20, 3 << 20, 4 << 20, 0, 0.5, None) == npa.NPA_OK
+
+
+def test_empty_calls_are_validated_no_ops(lib):
+    """batch = 0 or heads = 0 (and an SG latent with n*c = 0) computes nothing:
+    NPA_OK without touching any pointer (NULL allowed) and without a launch --
+    but the rest of the arguments are still checked first."""
+    strips = npa.make_halo(strips=4, p=0.3)
+    for field in ("batch", "heads"):
+        L = npa.make_layout(1, 2, 64, 32, 32)
+        setattr(L, field, 0)
+        assert lib.npa_attn_fwd(None, None, None, None, None, ctypes.byref(L), ctypes.byref(strips), None,
+                                None) == npa.NPA_OK
+        assert lib.npa_useful_flops(ctypes.byref(L), ctypes.byref(strips)) == 0
+        # still validated: a strip count that does not divide the map, an unsupported head size
+        assert _status(lib, L, npa.make_halo(strips=5, p=0.3)) == npa.NPA_ERR_SHAPE
+        L96 = npa.make_layout(1, 2, 96, 32, 32)
+        setattr(L96, field, 0)
+        assert _status(lib, L96, strips) == npa.NPA_ERR_UNSUPPORTED
+    for n, c in ((0, 4), (1, 0)):
+        assert lib.npa_sg_blend(None, None, None, n, c, 8, 8, 0.5, 4.0, None) == npa.NPA_OK
+    assert lib.npa_sg_blend(None, None, None, 0, 4, 8, 8, 0.5, 9.0, None) == npa.NPA_ERR_SHAPE
+    assert lib.npa_sg_blend(None, None, None, -1, 4, 8, 8, 0.5, 4.0, None) == npa.NPA_ERR_SHAPE
 
 
 def test_window_mode_needs_no_stale(lib):

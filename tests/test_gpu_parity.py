@@ -345,3 +345,32 @@ def test_joint_text_logits_take_the_robust_pass(d):
     ref = A.attention_tier1(q, k, v, None, None, H, W, spec)
     assert np.isfinite(got).all()
     assert np.abs(got - ref).max() <= 2e-2
+
+
+def test_empty_batch_and_heads_touch_nothing():
+    """batch = 0 or heads = 0 through the C ABI: NPA_OK, nothing is launched,
+    and an `out` buffer handed in anyway keeps its contents; the Python
+    binding and the SG blend accept empty tensors."""
+    import ctypes
+
+    lib = npa.load(build_if_missing=False)
+    H, W, d = 16, 16, 64
+    q = torch.randn(1, H * W, 2, d, device="cuda", dtype=torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    stream = torch.cuda.current_stream().cuda_stream
+    for field in ("batch", "heads"):
+        for h in (npa.make_halo(tile=(8, 8), halo=(4, 4)), npa.make_halo(strips=2, p=0.5)):
+            L = npa.make_layout(1, 2, d, H, W)
+            setattr(L, field, 0)
+            st = lib.npa_attn_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), q.data_ptr(), q.data_ptr(),
+                                  ctypes.byref(L), ctypes.byref(h), out.data_ptr(), stream)
+            assert st == npa.NPA_OK, lib.npa_last_error()
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    for shape in ((0, H * W, 2, d), (1, H * W, 0, d)):
+        e = torch.empty(shape, device="cuda", dtype=torch.bfloat16)
+        r = npa.attn_fwd(e, e.clone(), e.clone(), e.clone(), e.clone(), map_hw=(H, W), strips=2, p=0.5)
+        assert tuple(r.shape) == shape
+    x = torch.empty(0, 4, 8, 8, device="cuda")
+    assert tuple(npa.sg_blend(x, x.clone(), 0.5, 4.0).shape) == (0, 4, 8, 8)
+    torch.cuda.synchronize()
