@@ -374,3 +374,57 @@ def test_empty_batch_and_heads_touch_nothing():
     x = torch.empty(0, 4, 8, 8, device="cuda")
     assert tuple(npa.sg_blend(x, x.clone(), 0.5, 4.0).shape) == (0, 4, 8, 8)
     torch.cuda.synchronize()
+
+
+class _GpuRows:
+    """Read-only view of a device tensor [B, N, Hh, d] for the oracle: indexing
+    [b, token_indices, head] gathers those rows on the GPU and returns them as
+    float32 numpy (exact for bf16)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, key):
+        b, idx, j = key
+        sel = torch.as_tensor(np.asarray(idx, dtype=np.int64), device=self.t.device)
+        return self.t[b, sel, j].float().cpu().numpy()
+
+
+@pytest.mark.parametrize("spec", [A.Windows(64, 64, 16, 16), A.Strips(8, p=0.3)])
+def test_slice_at_the_32bit_offset_limit(spec):
+    """One (batch, head) slice spanning 2^31 - 1920 bytes, just under the bf16
+    kernel's 2^31 - 16 byte addressing limit: a 1024x1024 map whose tokens are
+    2 KiB apart (head 0 of 16 used; the other 15 heads' rows are NaN padding
+    that must never be read).  Sampled queries in the first, a middle and the
+    last tile or strip (the largest offsets) against the oracle."""
+    H = W = 1024
+    N, d, pad_heads = H * W, 64, 16
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+
+    def tensor(like=None):
+        full = torch.full((1, N, pad_heads, d), float("nan"), device="cuda", dtype=torch.bfloat16)
+        if like is None:
+            full[:, :, 0] = torch.randn((1, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+        else:
+            full[:, :, 0] = (like[:, :, 0].float()
+                             + 0.05 * torch.randn((1, N, d), generator=gen, device="cuda")).to(torch.bfloat16)
+        return full[:, :, :1]  # strides (N*1024, 1024, 64, 1)
+
+    q, k, v = tensor(), tensor(), tensor()
+    strips = isinstance(spec, A.Strips)
+    ks, vs = (tensor(k), tensor(v)) if strips else (None, None)
+    out = tensor()
+    L = npa.make_layout(1, 1, d, H, W, strides=q.stride()[:3])
+    assert npa.useful_flops(L, npa.make_halo(**_kw(spec))) > 0
+    npa.attn_fwd(q, k, v, ks, vs, map_hw=(H, W), out=out, **_kw(spec))
+    torch.cuda.synchronize()
+    rows = [0, 1, H // 2, H - 2, H - 1]
+    sample = np.array(sorted({r * W + c for r in rows for c in (0, 5, W // 2, W - 6, W - 1)}), dtype=np.int64)
+    ref = A.attention_tier1(_GpuRows(q), _GpuRows(k), _GpuRows(v), None if ks is None else _GpuRows(ks),
+                            None if vs is None else _GpuRows(vs), H, W, spec, query_tokens=sample,
+                            heads=[(0, 0)])
+    got = out[0, torch.as_tensor(sample, device="cuda"), 0].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref[0, sample, 0]).max()
+    assert np.isfinite(got).all()
+    assert err <= ATOL["bf16"], err
