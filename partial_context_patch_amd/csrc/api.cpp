@@ -2,6 +2,7 @@
 // useful-flop accounting, kernel selection and launch, error reporting.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -40,6 +41,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int32_t halo_from_p(float p, int32_t s) {
   const double v = std::ceil((double)p * (double)s - 1e-6 * (double)s);
   return v < 0.0 ? 0 : (int32_t)v;
+}
+
+// Compute units of the current device (queried once per device), 0 if unknown.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 // Validate the layout and halo; build the plan parameters.
@@ -183,7 +203,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   int block_m;
   if (L->dtype == NPA_BF16) {
     esize = 2;
-    block_m = npa::attn_bf16_block_m(L->head_dim);
+    block_m = npa::attn_bf16_block_m(L->head_dim, false);
   } else if (L->dtype == NPA_F32) {
     esize = 4;
     block_m = npa::attn_f32_block_m(L->head_dim);
@@ -236,10 +256,24 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   a.Hh = L->heads;
   a.g = g;
   const int32_t nq = npa::tile_queries(g);
-  a.qblocks = (nq + block_m - 1) / block_m;
-  a.text_qblocks = (g.T + block_m - 1) / block_m;
-  const int64_t text_blocks = (int64_t)L->batch * L->heads * a.text_qblocks;
-  const int64_t nblocks = text_blocks + (int64_t)L->batch * L->heads * g.n_img * a.qblocks;
+  int64_t text_blocks = 0, nblocks = 0;
+  auto grid = [&](int bm) {
+    a.qblocks = (nq + bm - 1) / bm;
+    a.text_qblocks = (g.T + bm - 1) / bm;
+    text_blocks = (int64_t)L->batch * L->heads * a.text_qblocks;
+    nblocks = text_blocks + (int64_t)L->batch * L->heads * g.n_img * a.qblocks;
+  };
+  grid(block_m);
+  // bf16: a grid that would not fill the GPU's workgroup slots twice runs in
+  // the small-launch shape (twice the workgroups, each half as long)
+  bool small = false;
+  if (L->dtype == NPA_BF16) {
+    const int cus = cu_count();
+    if (cus > 0 && nblocks < 2ll * cus * npa::attn_bf16_per_cu(L->head_dim, false)) {
+      small = true;
+      grid(npa::attn_bf16_block_m(L->head_dim, true));
+    }
+  }
   if (nblocks >= (int64_t(1) << 31))
     return fail(NPA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)nblocks);
   a.nblocks = (int32_t)nblocks;
@@ -251,7 +285,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
   a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = (L->dtype == NPA_BF16) ? npa::launch_attn_bf16(a, L->head_dim, block_m, s)
+  const hipError_t e = (L->dtype == NPA_BF16) ? npa::launch_attn_bf16(a, L->head_dim, small, s)
                                               : npa::launch_attn_f32(a, L->head_dim, block_m, s);
   if (e != hipSuccess) return fail(NPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

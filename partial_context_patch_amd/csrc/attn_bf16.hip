@@ -61,36 +61,35 @@ constexpr int kBN = 64;                  // keys per LDS block
 constexpr uint32_t kOOB = 0x7FFFFFF0u;   // byte offset past every buffer's range
 constexpr float kOverflow = 1.152921504606846976e18f;  // 2^60
 
-// Per head size: NT = 32-query column tiles per wave, WAVES = waves per
-// workgroup (all sharing the workgroup's K/V tiles), MINB = workgroups per CU
-// the register budget is sized for (two waves per SIMD either way).  d = 128
-// takes eight waves: its K/V tiles are twice as large per query, and sharing
-// them among more queries halves the copies per MFMA.
-#ifndef NPA_NT64
-#define NPA_NT64 2
-#endif
-#ifndef NPA_WAVES64
-#define NPA_WAVES64 4
-#endif
-#ifndef NPA_NT128
-#define NPA_NT128 1
-#endif
-#ifndef NPA_WAVES128
-#define NPA_WAVES128 8
-#endif
-template <int D>
+// Workgroup shape per head size: NT = 32-query column tiles per wave, WAVES =
+// waves per workgroup (all sharing the workgroup's K/V tiles), MINB =
+// workgroups per CU the register budget is sized for.
+//   regular (SMALL = false), two waves per SIMD: d = 64 takes 4 waves of 64
+//     queries; d = 128 takes 8 waves of 32 -- its K/V tiles are twice as large
+//     per query, and sharing them among more queries halves the copies per
+//     MFMA.  256 queries per workgroup either way.
+//   small-launch (SMALL = true): 128 queries per workgroup (4 waves of 32),
+//     for calls whose regular grid would not fill the GPU twice: twice the
+//     workgroups, each half as long, so the launch ends evenly; at d = 64 the
+//     smaller register set fits three waves per SIMD.  On large grids it is
+//     ~7% slower (each K/V tile serves half the queries).
+template <int D, bool SMALL>
 struct Cfg;
 template <>
-struct Cfg<64> {
-  static constexpr int NT = NPA_NT64;
-  static constexpr int WAVES = NPA_WAVES64;
-  static constexpr int MINB = 8 / WAVES;
+struct Cfg<64, false> {
+  static constexpr int NT = 2, WAVES = 4, MINB = 2;
 };
 template <>
-struct Cfg<128> {
-  static constexpr int NT = NPA_NT128;
-  static constexpr int WAVES = NPA_WAVES128;
-  static constexpr int MINB = 8 / WAVES;
+struct Cfg<128, false> {
+  static constexpr int NT = 1, WAVES = 8, MINB = 1;
+};
+template <>
+struct Cfg<64, true> {
+  static constexpr int NT = 1, WAVES = 4, MINB = 3;
+};
+template <>
+struct Cfg<128, true> {
+  static constexpr int NT = 1, WAVES = 4, MINB = 2;
 };
 
 // j / d for 0 <= j < 2^24 via a float reciprocal and one correction step.
@@ -195,13 +194,14 @@ __device__ __forceinline__ float max16(const f32x16& a) {
 // single-run cursor).
 constexpr int kModeJoint = 2;
 
-template <int D, int MODE, bool PARTIAL>
-__global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_kernel(const AttnArgs a) {
+template <int D, int MODE, bool PARTIAL, bool SMALL>
+__global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB)) void attn_bf16_kernel(
+    const AttnArgs a) {
   constexpr bool kWin = MODE != NPA_MODE_STRIPS;  // map tiles are 2-D windows
   constexpr bool kRuns = MODE != NPA_MODE_WINDOW;  // more than one key run per tile
-  constexpr int kWaves = Cfg<D>::WAVES;
+  constexpr int kWaves = Cfg<D, SMALL>::WAVES;
   constexpr int kThreads = 64 * kWaves;
-  constexpr int NT = Cfg<D>::NT;
+  constexpr int NT = Cfg<D, SMALL>::NT;
   constexpr int ROWS = 32 * NT;
   constexpr int BM = kWaves * ROWS;
   constexpr int KS = D / 16;    // k-steps of S^T
@@ -600,37 +600,49 @@ __global__ __launch_bounds__(64 * Cfg<D>::WAVES, Cfg<D>::MINB) void attn_bf16_ke
 
 }  // namespace
 
-int attn_bf16_block_m(int head_dim) {
-  if (head_dim == 64) return Cfg<64>::WAVES * 32 * Cfg<64>::NT;
-  if (head_dim == 128) return Cfg<128>::WAVES * 32 * Cfg<128>::NT;
+int attn_bf16_block_m(int head_dim, bool small) {
+  if (head_dim == 64) return small ? 32 * Cfg<64, true>::WAVES * Cfg<64, true>::NT : 32 * Cfg<64, false>::WAVES * Cfg<64, false>::NT;
+  if (head_dim == 128) return small ? 32 * Cfg<128, true>::WAVES * Cfg<128, true>::NT : 32 * Cfg<128, false>::WAVES * Cfg<128, false>::NT;
   return 0;
 }
 
-template <int D, int MODE>
-void launch_dm(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid(a.nblocks), block(64 * Cfg<D>::WAVES);
-  if (a.partial)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, true>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, false>), grid, block, 0, st, a);
+int attn_bf16_per_cu(int head_dim, bool small) {
+  if (head_dim == 64) return small ? Cfg<64, true>::MINB : Cfg<64, false>::MINB;
+  if (head_dim == 128) return small ? Cfg<128, true>::MINB : Cfg<128, false>::MINB;
+  return 0;
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int /*block_m*/, hipStream_t st) {
+template <int D, int MODE, bool SMALL>
+void launch_dm(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.nblocks), block(64 * Cfg<D, SMALL>::WAVES);
+  if (a.partial)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, true, SMALL>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, MODE, false, SMALL>), grid, block, 0, st, a);
+}
+
+template <int D, bool SMALL>
+void launch_d(const AttnArgs& a, hipStream_t st) {
   const int mode = a.g.mode == NPA_MODE_STRIPS ? NPA_MODE_STRIPS : (a.g.T > 0 ? kModeJoint : NPA_MODE_WINDOW);
+  if (mode == NPA_MODE_STRIPS)
+    launch_dm<D, NPA_MODE_STRIPS, SMALL>(a, st);
+  else if (mode == NPA_MODE_WINDOW)
+    launch_dm<D, NPA_MODE_WINDOW, SMALL>(a, st);
+  else
+    launch_dm<D, kModeJoint, SMALL>(a, st);
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool small, hipStream_t st) {
   if (head_dim == 64) {
-    if (mode == NPA_MODE_STRIPS)
-      launch_dm<64, NPA_MODE_STRIPS>(a, st);
-    else if (mode == NPA_MODE_WINDOW)
-      launch_dm<64, NPA_MODE_WINDOW>(a, st);
+    if (small)
+      launch_d<64, true>(a, st);
     else
-      launch_dm<64, kModeJoint>(a, st);
+      launch_d<64, false>(a, st);
   } else {
-    if (mode == NPA_MODE_STRIPS)
-      launch_dm<128, NPA_MODE_STRIPS>(a, st);
-    else if (mode == NPA_MODE_WINDOW)
-      launch_dm<128, NPA_MODE_WINDOW>(a, st);
+    if (small)
+      launch_d<128, true>(a, st);
     else
-      launch_dm<128, kModeJoint>(a, st);
+      launch_d<128, false>(a, st);
   }
   return hipGetLastError();
 }

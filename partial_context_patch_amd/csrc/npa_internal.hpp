@@ -190,9 +190,11 @@ struct SgArgs {
 };
 
 // Launchers (return the HIP error of the launch).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int block_m, hipStream_t st);
+// bf16: `small` selects the small-launch workgroup shape (see attn_bf16.hip).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool small, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int block_m, hipStream_t st);
-int attn_bf16_block_m(int head_dim);  // queries per workgroup, 0 if unsupported
+int attn_bf16_block_m(int head_dim, bool small);  // queries per workgroup, 0 if unsupported
+int attn_bf16_per_cu(int head_dim, bool small);   // workgroups resident per CU
 int attn_f32_block_m(int head_dim);
 hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st);
 hipError_t launch_asg_blend(const float* eps, const float* ref, const float* mask, float* out,

@@ -428,3 +428,31 @@ def test_slice_at_the_32bit_offset_limit(spec):
     err = np.abs(got - ref[0, sample, 0]).max()
     assert np.isfinite(got).all()
     assert err <= ATOL["bf16"], err
+
+
+# Full compares on small ragged maps with enough (batch, head) pairs that the
+# grid fills the GPU at least twice over, so the regular workgroup shape runs
+# (the small cases above, and small calls generally, take the small-launch
+# shape).  Queries per regular workgroup: 256 at d = 64 and d = 128.
+REGULAR = [
+    # (H, W, B, Hh, d, spec)
+    (24, 20, 2, 172, 64, A.Strips(3, halo_rows=3)),
+    (40, 36, 1, 90, 128, A.Windows(20, 12, 4, 7)),
+    (16, 16, 2, 130, 64, A.Windows(8, 8, 2, 2, 7)),
+]
+
+
+@pytest.mark.parametrize("H,W,B,Hh,d,spec", REGULAR)
+def test_regular_shape_full_compare(H, W, B, Hh, d, spec):
+    T = A.text_tokens(spec)
+    tiles = list(A.iter_tiles(H, W, spec))
+    n_map = len(tiles) - (1 if T else 0)
+    nq = len(tiles[0][0])
+    grid = B * Hh * (n_map * -(-nq // 256) + (-(-T // 256) if T else 0))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_cu = 2 if d == 64 else 1
+    assert grid >= 2 * cus * per_cu, "case too small to run the regular workgroup shape"
+    inp = WL.attention_inputs(B, Hh, d, H, W, seed=77, dtype="bf16", text_tokens=T)
+    got = _run(inp, H, W, spec, "bf16")
+    ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec)
+    assert np.abs(got - ref).max() <= ATOL["bf16"]
