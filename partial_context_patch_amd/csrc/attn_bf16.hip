@@ -4,14 +4,15 @@
 // each query tile -- own strip fresh plus a stale halo of neighbour rows
 // ("Partially Conditioned Patch Parallelism ...", "What carries the
 // argument"), or a clipped overlapping window ("ScaleDiff ...", "Approach").
-// Flash-style: one pass over the tile's keys with an online softmax, so the
-// score matrix never leaves registers and K/V are read in place from the
+// Flash-style: one pass over the tile's keys with a fixed softmax shift, so
+// the score matrix never leaves registers and K/V are read in place from the
 // fresh and stale buffers (never concatenated).
 //
-// Workgroup = WAVES waves (4 at d = 64, 8 at d = 128); each wave owns
-// ROWS = 32*NT queries of one tile.  The workgroup walks the tile's keys in
-// blocks of 64 staged through a double-buffered LDS tile (one barrier per
-// block); each wave consumes a block as two 32-key sub-blocks.
+// Workgroup = WAVES waves (regular shape: 4 at d = 64, 8 at d = 128, 256
+// queries; small-launch shape: 4 waves, 128 queries); each wave owns ROWS =
+// 32*NT queries of one tile.  The workgroup walks the tile's keys in blocks
+// of 64 staged through a double-buffered LDS tile (one barrier per block);
+// each wave consumes a block as two 32-key sub-blocks.
 //
 // MFMA orientation (v_mfma_f32_32x32x16_bf16, lane l: column l%32, half g=l/32):
 //   S^T = K * Q^T   A = K rows (keys),  B = Q^T (queries in columns)
@@ -29,9 +30,10 @@
 //     the product is already in the exp2 domain;
 //   * the running shift -m enters as the C operand of the first S^T MFMA
 //     (a persistent register tile), so p = exp2(acc) with no subtraction;
-//   * the shift is the exact row max of the first 32 keys and is raised only
-//     when a row sum would exceed 2^60 (checked from the sum itself), so the
-//     common path has no max, no rescale of O and no branch per query;
+//   * the shift is the exact row max of the first 32 keys and never moves, so
+//     the common path has no max, no rescale of O and no branch per query; if
+//     a row sum ends outside [1, 2^60] (checked from the sums themselves) the
+//     workgroup computes the true row maxima and runs the tile again with them;
 //   * row sums come from v_dot2c_f32_bf16 on the packed bf16 P, i.e. the
 //     denominator sums exactly the weights the numerator uses.
 // Loads and stores go through buffer descriptors: out-of-range keys and

@@ -31,11 +31,30 @@ KERNEL_SOURCES = ("csrc/attn_bf16.hip", "csrc/npa_internal.hpp")
 COPY_BYTES = 512 << 20
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """The source with // comments, trailing blanks and blank lines removed, so
+    that an edit to comments alone keeps the hash (string literals in these
+    kernel sources hold no //)."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return "\n".join(lines)
+
+
+def kernel_source_hash(sources: Optional[Dict[str, str]] = None) -> str:
+    """Hash of the attention kernel's code (comments excluded) -- a counter
+    summary applies only to the code it was taken on.  `sources` maps the
+    KERNEL_SOURCES paths to their text (default: the files on disk)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(f.read())
+        if sources is not None:
+            text = sources[rel]
+        else:
+            with open(os.path.join(HERE, rel), encoding="utf-8") as f:
+                text = f.read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 
