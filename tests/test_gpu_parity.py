@@ -456,3 +456,42 @@ def test_regular_shape_full_compare(H, W, B, Hh, d, spec):
     got = _run(inp, H, W, spec, "bf16")
     ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec)
     assert np.abs(got - ref).max() <= ATOL["bf16"]
+
+
+def test_calls_replay_from_a_hip_graph():
+    """npa_attn_fwd and npa_sg_blend captured into one HIP graph: every replay
+    (with eager work and synchronisations between replays) reproduces the
+    eager result bit for bit."""
+    H = W = 32
+    spec = A.Windows(8, 8, 4, 4)
+    inp = WL.attention_inputs(1, 2, 64, H, W, seed=31, dtype="bf16")
+    q, k, v = (_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    x, r = (torch.from_numpy(a).cuda() for a in WL.sg_inputs(4, 40, 56, seed=32))
+    out, sg_out = torch.empty_like(q), torch.empty_like(x)
+
+    def step():
+        npa.attn_fwd(q, k, v, map_hw=(H, W), out=out, **_kw(spec))
+        npa.sg_blend(x, r, 0.5, 4.0, out=sg_out)
+
+    step()  # eager reference (also warms the library's per-device state)
+    torch.cuda.synchronize()
+    ref_attn, ref_sg = out.clone(), sg_out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        out.zero_()
+        sg_out.zero_()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        sg_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_attn), f"replay {i}: attention differs"
+        assert torch.equal(sg_out, ref_sg), f"replay {i}: SG blend differs"
+        _ = (q.float() * 2).sum().item()  # eager work between replays
