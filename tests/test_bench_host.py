@@ -20,3 +20,17 @@ def test_world_size_above_one_is_refused():
                        timeout=120, env=env)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_times_the_oracle_on_a_sample():
+    """The cpu_baseline leg runs the oracle on whole (batch, head, query tile)
+    units of the workload and reports its useful-flop rate and thread count."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from partial_context_patch_amd import workloads as WL
+
+    name = "pcpp_tiny_fp32"
+    res = bench.cpu_baseline(name, WL.workload_inputs(name), budget_s=0.5)
+    assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
+    assert res["value"] > 0 and res["cores"] >= 1
+    assert "units of 8" in res["sample"]  # 2 heads x 4 strips
