@@ -10,20 +10,25 @@
 //
 // Workgroup = WAVES waves (regular shape: 4 at d = 64, 8 at d = 128, 256
 // queries; small-launch shape: 4 waves, 128 queries); each wave owns ROWS =
-// 32*NT queries of one tile.  The workgroup walks the tile's keys in blocks
+// 16*NT queries of one tile.  The workgroup walks the tile's keys in blocks
 // of 64 staged through a double-buffered LDS tile (one barrier per block);
-// each wave consumes a block as two 32-key sub-blocks.
+// each wave consumes a block as two 32-key steps.
 //
-// MFMA orientation (v_mfma_f32_32x32x16_bf16, lane l: column l%32, half g=l/32):
-//   S^T = K * Q^T   A = K rows (keys),  B = Q^T (queries in columns)
-//   O^T = V^T * P^T A = V^T (head dims), B = P^T
-// With scores transposed, each lane holds 16 keys of ONE query per sub-block:
-// row reductions are in-lane plus one v_permlane32_swap, and rescaling O^T by
-// a per-query factor is in-lane.  K rows are loaded in the order
-// pi(r) = r with bits 2 and 3 swapped, which puts accumulator entries j=0..7 of
-// lane half g on keys 8g..8g+7 -- the B-operand layout of the PV product -- so P
-// goes from the score accumulator to the MFMA operand with no lane movement.
-// V^T fragments come from the row-major V tile through ds_read_b64_tr_b16.
+// MFMA orientation (v_mfma_f32_16x16x32_bf16; lane l: column l%16, group
+// g4 = l/16; A and B hold k = 8*g4 .. +8, D holds rows 4*g4 .. +4):
+//   S^T = K * Q^T   A = K rows (16 keys),  B = Q^T (16 queries in columns)
+//   O^T = V^T * P^T A = V^T (16 head dims), B = P^T (32 keys)
+// With scores transposed, each lane holds keys of ONE query: row reductions
+// are in-lane plus two lane swaps (v_permlane16_swap, v_permlane32_swap), and
+// rescaling O^T by a per-query factor is in-lane.  Of the 16x16x32 and
+// 32x32x16 bf16 MFMAs the smaller one touches half the accumulator registers
+// per flop; on random bf16 data it sustains ~14% more under the board's power
+// limit.  Within each 32-key step the K rows of the two 16-key score tiles
+// are permuted (tile h, row r <- key 8*(r/4) + 4h + r%4), which puts the two
+// tiles' accumulator entries of lane group g4 on keys 8*g4 .. 8*g4+7 -- the
+// B-operand layout of the PV product -- so P goes from the score accumulators
+// to the MFMA operand with no lane movement.  V^T fragments come from the
+// row-major V tile through two ds_read_b64_tr_b16 of four key rows each.
 //
 // Softmax arithmetic is kept off the VALU wherever the MFMA can carry it:
 //   * Q is multiplied by scale*log2(e) once at load (re-rounded to bf16), so
@@ -50,7 +55,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,7 +67,7 @@ constexpr int kBN = 64;                  // keys per LDS block
 constexpr uint32_t kOOB = 0x7FFFFFF0u;   // byte offset past every buffer's range
 constexpr float kOverflow = 1.152921504606846976e18f;  // 2^60
 
-// Workgroup shape per head size: NT = 32-query column tiles per wave, WAVES =
+// Workgroup shape per head size: NT = 16-query column tiles per wave, WAVES =
 // waves per workgroup (all sharing the workgroup's K/V tiles), MINB =
 // workgroups per CU the register budget is sized for.
 //   regular (SMALL = false), two waves per SIMD: d = 64 takes 4 waves of 64
@@ -79,19 +83,19 @@ template <int D, bool SMALL>
 struct Cfg;
 template <>
 struct Cfg<64, false> {
-  static constexpr int NT = 2, WAVES = 4, MINB = 2;
+  static constexpr int NT = 4, WAVES = 4, MINB = 2;
 };
 template <>
 struct Cfg<128, false> {
-  static constexpr int NT = 1, WAVES = 8, MINB = 1;
+  static constexpr int NT = 2, WAVES = 8, MINB = 1;
 };
 template <>
 struct Cfg<64, true> {
-  static constexpr int NT = 1, WAVES = 4, MINB = 3;
+  static constexpr int NT = 2, WAVES = 4, MINB = 3;
 };
 template <>
 struct Cfg<128, true> {
-  static constexpr int NT = 1, WAVES = 4, MINB = 2;
+  static constexpr int NT = 2, WAVES = 4, MINB = 2;
 };
 
 // j / d for 0 <= j < 2^24 via a float reciprocal and one correction step.
@@ -102,24 +106,29 @@ __device__ __forceinline__ int fast_div(int j, int d, float inv) {
   return q;
 }
 
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
 }
-
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(r[0]) + __int_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+__device__ __forceinline__ float max4(const f32x4& a) { return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// 16-byte chunk permutation of LDS row r.  With it, the 8 lanes of each
-// ds_read_b128 quarter (K fragments: rows {0..3, 8..11} + 4k, one chunk) and
+// 16-byte chunk permutation of LDS row r.  With it, each 8 lanes of a
+// ds_read_b128 (K fragments: rows {0..3, 8..11} + 16j + 4h, one chunk) and
 // the 16 lanes of each ds_read_b64_tr_b16 quarter (V fragments: 4 consecutive
 // rows x 2 adjacent chunks) hit 8 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
@@ -143,51 +152,38 @@ __device__ __forceinline__ int run_token(const Run& r, int j, float inv_len) {
   return r.start + row * r.pitch + (j - row * r.row_len);
 }
 
-// exp2 of 16 accumulator entries, packed to bf16 pairs for the PV operand;
-// returns s plus the sum of the packed (bf16) weights.
-__device__ __forceinline__ float exp_pack(const f32x16& acc, float shift, bf16x8& p0, bf16x8& p1, float s) {
-  f32x8 a, b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = __builtin_amdgcn_exp2f(acc[i] - shift);
-    b[i] = __builtin_amdgcn_exp2f(acc[8 + i] - shift);
-  }
-  p0 = __builtin_convertvector(a, bf16x8);
-  p1 = __builtin_convertvector(b, bf16x8);
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+// exp2 of the 8 accumulator entries of one lane for a 32-key step (tiles 0
+// and 1), packed to bf16 in key order as the PV B operand; returns s plus the
+// sum of the packed (bf16) weights.
+__device__ __forceinline__ float exp_pack(const f32x4& a0, const f32x4& a1, float shift, bf16x8& p, float s) {
+  f32x8 e;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * i], p1[2 * i + 1]}, one, s, false);
+    e[i] = __builtin_amdgcn_exp2f(a0[i] - shift);
+    e[4 + i] = __builtin_amdgcn_exp2f(a1[i] - shift);
   }
+  p = __builtin_convertvector(e, bf16x8);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, s, false);
   return s;
 }
 
 // Same without a shift argument (the common path: the shift is inside acc).
-__device__ __forceinline__ float exp_pack0(const f32x16& acc, bf16x8& p0, bf16x8& p1, float s) {
-  f32x8 a, b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = __builtin_amdgcn_exp2f(acc[i]);
-    b[i] = __builtin_amdgcn_exp2f(acc[8 + i]);
-  }
-  p0 = __builtin_convertvector(a, bf16x8);
-  p1 = __builtin_convertvector(b, bf16x8);
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+__device__ __forceinline__ float exp_pack0(const f32x4& a0, const f32x4& a1, bf16x8& p, float s) {
+  f32x8 e;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[2 * i], p0[2 * i + 1]}, one, s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[2 * i], p1[2 * i + 1]}, one, s, false);
+    e[i] = __builtin_amdgcn_exp2f(a0[i]);
+    e[4 + i] = __builtin_amdgcn_exp2f(a1[i]);
   }
+  p = __builtin_convertvector(e, bf16x8);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, s, false);
   return s;
 }
 
-__device__ __forceinline__ float max16(const f32x16& a) {
-  float m = fmaxf(a[0], a[1]);
-#pragma unroll
-  for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(a[i], a[i + 1]));
-  return m;
-}
 
 // PARTIAL: some key run of the plan is not a multiple of 64 keys, so some
 // blocks end inside the padding and need masking (instantiated only then).
@@ -204,10 +200,10 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   constexpr int kWaves = Cfg<D, SMALL>::WAVES;
   constexpr int kThreads = 64 * kWaves;
   constexpr int NT = Cfg<D, SMALL>::NT;
-  constexpr int ROWS = 32 * NT;
+  constexpr int ROWS = 16 * NT;
   constexpr int BM = kWaves * ROWS;
-  constexpr int KS = D / 16;    // k-steps of S^T
-  constexpr int DT = D / 32;    // 32-wide head-dim tiles of O^T
+  constexpr int KS = D / 32;    // k-steps of S^T (32 head dims each)
+  constexpr int DT = D / 16;    // 16-wide head-dim tiles of O^T
   constexpr int LDR = D;        // LDS row pitch in elements (unpadded; chunks XOR-swizzled)
   constexpr int CPR = D / 8;    // 16-byte chunks per key row
   constexpr int CH = kBN * CPR / kThreads;  // DMA instructions per thread per tile
@@ -224,7 +220,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   // wave index as a uniform value: everything derived from it (LDS tile slots,
   // the DMA destinations) stays in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int g4 = lane >> 4, l16 = lane & 15;
 
   const BlockCoord bc = decode_block(a, blockIdx.x, true);
   const int qb = bc.qb, tile = bc.tile, head = bc.head, b = bc.b;
@@ -244,12 +240,12 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   const rsrc_t ro = make_rsrc((__bf16*)a.o + bh, a.range_bytes);
 
   // ---- Q^T fragments, pre-multiplied by scale*log2(e):
-  //      lane (query l32, half g) holds dims 16*ks + 8g .. +8
+  //      lane (query l16, group g4) holds dims 32*ks + 8*g4 .. +8
   bf16x8 qf[NT][KS];
   uint32_t qoff[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int qi = qb * BM + wave * ROWS + nt * 32 + l32;
+    const int qi = qb * BM + wave * ROWS + nt * 16 + l16;
     uint32_t off = kOOB;
     if (qi < nq) {
       int tok;
@@ -264,7 +260,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     qoff[nt] = off;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32 + g * 16, 0, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64 + g4 * 16, 0, 0);
       f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] *= a.c;
@@ -372,16 +368,35 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     for (int j = 0; j < 2 * CH; ++j) fetch_part(j >> 1, j & 1, off[j >> 1], skd, svd);
   };
 
-  f32x16 o[DT][NT];
-  f32x16 shift[NT];  // -m in every entry: C operand of the first S^T MFMA
+  f32x4 o[DT][NT];
+  f32x4 shift[NT];  // -m in every entry: C operand of the first S^T MFMA
   float l[NT];
 
-  // row of the K tile this lane feeds into the S^T product: bits 2,3 of l32 swapped
-  const int krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  // ds_read_b64_tr_b16 source address pattern for the V^T fragments
-  const int vkey = 8 * g + ((lane & 15) >> 2);
-  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // K row this lane feeds into the S^T tile h (0, 1) of a 32-key step: rows
+  // are permuted so that the tiles' accumulator entries of lane group g4 are
+  // the step's keys 8*g4 + 4h .. +4 -- together the B-operand layout of the
+  // PV product (keys 8*g4 .. +8).
+  const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
+  // ds_read_b64_tr_b16 source pattern for the V^T fragments: within each
+  // 16-lane group, lanes 4r..4r+3 address 16 consecutive dims of key row r
+  const int vrow = 8 * g4 + (l16 >> 2);
+  const int vcol = 4 * (l16 & 3);
   const int nkb = pad_blocks(tr.nk[0]) + pad_blocks(tr.nk[1]) + pad_blocks(tr.nk[2]);
+
+  // S^T of 32-key step s of the block in skb: tiles h = 0, 1 (C operand: the
+  // shift tile, or zero for raw scores)
+  auto scores_raw = [&](const __bf16* skb, int s, f32x4 (&sc)[2][NT], bool raw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int row = 32 * s + krow0 + 4 * h;
+        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((4 * ks + g4) ^ swz(row)) * 8)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          sc[h][nt] = mfma16(kf, qf[nt][ks], ks == 0 ? (raw ? f32x4{} : shift[nt]) : sc[h][nt]);
+      }
+  };
 
   // Exact row max of the whole tile (the rare second pass only): S^T with a
   // zero shift, reduced over every key.
@@ -397,22 +412,17 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
         fetch(skn, svn);
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16 s[NT];
+      for (int s = 0; s < 2; ++s) {
+        f32x4 sc[2][NT];
+        scores_raw(skb, s, sc, true);
+        const int t = valid - 32 * s - 8 * g4;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int row = mt * 32 + krow;
-          const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[nt] = mfma(kf, qf[nt][ks], ks == 0 ? f32x16{} : s[nt]);
-        }
-        const int base = valid - mt * 32;
-        const int t = base - 8 * g;
+          for (int i = 0; i < 4; ++i)
+            if (4 * h + i < t)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((j < 8 ? j : j + 8) < t)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) mx[nt] = fmaxf(mx[nt], s[nt][j]);
+              for (int nt = 0; nt < NT; ++nt) mx[nt] = fmaxf(mx[nt], sc[h][nt][i]);
       }
     };
     cursor_reset();
@@ -422,7 +432,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
       if (kb + 1 < nkb) block(kb + 1, sk1, sk0, sv0);
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) mx[nt] = pair_max(mx[nt]);
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = quad_max(mx[nt]);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the tiles are free again
   };
@@ -432,11 +442,12 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   // of the first 32 keys.  preset=true: the shift was set beforehand (the true
   // row max of the tile).
   //
-  // Each 64-key block is one straight-line body, specialised at compile time
-  // for the first block (FIRST: scores unshifted, the max is taken): the score
-  // MFMAs of both 32-key halves are issued before the first half's exp work,
-  // so the second half's MFMAs run while the VALU does the first half's
-  // softmax.  Blocks that end inside a run's padding take the same body.
+  // Each 64-key block is one straight-line body of two 32-key steps,
+  // specialised at compile time for the first block (FIRST: scores unshifted,
+  // the max is taken): the score MFMAs of both steps are issued before the
+  // first step's exp work, so the second step's MFMAs run while the VALU does
+  // the first step's softmax.  Blocks that end inside a run's padding take the
+  // same body.
   auto block = [&](int kb, const __bf16* skb, const __bf16* svb, __bf16* skn, __bf16* svn,
                    auto first_tag) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
@@ -452,92 +463,81 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
       fetch(skn, svn);
     }
 
-    // S^T of half mt in the exp2 domain, shifted by the C operand (FIRST:
-    // the shift is zero, so these are the raw scores)
-    auto scores = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
+    // Keys past the end of their run: entry i of tile h in lane group g4 is
+    // key 8*g4 + 4h + i of step s; their scores become -inf.  Only blocks that
+    // end inside a run's padding take this step, between the scheduled
+    // regions, so full blocks and partial ones share one body.
+    auto mask = [&](int s, f32x4 (&sc)[2][NT]) __attribute__((always_inline)) {
+      const int t = valid - 32 * s - 8 * g4;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int row = mt * 32 + krow;
-        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((2 * ks + g) ^ swz(row)) * 8)];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sc[nt] = mfma(kf, qf[nt][ks], ks == 0 ? shift[nt] : sc[nt]);
-      }
+        for (int i = 0; i < 4; ++i)
+          if (4 * h + i >= t)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) sc[h][nt][i] = -INFINITY;
     };
-    // Keys past the end of their run: entry j of lane half g is key 8g + j
-    // (j < 8) or 8g + j + 8 (j >= 8) of half mt; their scores become -inf.
-    // Only blocks that end inside a run's padding take this step, between the
-    // scheduled regions, so full blocks and partial ones share one body.
-    auto mask = [&](int mt, f32x16 (&sc)[NT]) __attribute__((always_inline)) {
-      const int t = valid - mt * 32 - 8 * g;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((j < 8 ? j : j + 8) >= t)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) sc[nt][j] = -INFINITY;
-    };
-    // O^T += V^T P^T over half mt
-    auto pv = [&](int mt, const bf16x8 (&p0)[NT], const bf16x8 (&p1)[NT]) __attribute__((always_inline)) {
+    // O^T += V^T P^T over step s: per 16-dim tile one V^T fragment (keys
+    // 8*g4 .. +8 of the step, from two transposed reads of four key rows)
+    auto pv = [&](int s, const bf16x8 (&p)[NT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
+        const int r0 = 32 * s + vrow, r1 = r0 + 4;
+        const int col = 16 * dt + vcol;  // multiple of 4: one 8-byte half of a chunk
+        const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
+        const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
+        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int r0 = mt * 32 + 16 * h2 + vkey, r1 = r0 + 4;
-          const int col = 32 * dt + vdim;  // multiple of 4: one 8-byte half of a chunk
-          const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
-          const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
-          const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma(vf, h2 ? p1[nt] : p0[nt], o[dt][nt]);
-        }
+        for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma16(vf, p[nt], o[dt][nt]);
       }
     };
 
-    f32x16 s0[NT], s1[NT];
-    bf16x8 pa0[NT], pa1[NT], pb0[NT], pb1[NT];
-    scores(0, s0);
+    f32x4 s0[2][NT], s1[2][NT];
+    bf16x8 pa[NT], pb[NT];
+    scores_raw(skb, 0, s0, FIRST);
     if (part) mask(0, s0);
     if (FIRST) {
-      // the exact row max of the first 32 keys becomes the shift; half 1 then
+      // the exact row max of the first 32 keys becomes the shift; step 1 then
       // takes the ordinary path with the shift inside its MFMA
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float m = pair_max(max16(s0[nt]));
-        l[nt] = exp_pack(s0[nt], m, pa0[nt], pa1[nt], l[nt]);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) shift[nt][j] = -m;
+        float m = fmaxf(max4(s0[0][nt]), max4(s0[1][nt]));
+        m = quad_max(m);
+        l[nt] = exp_pack(s0[0][nt], s0[1][nt], m, pa[nt], l[nt]);
+        shift[nt] = f32x4{-m, -m, -m, -m};
       }
-      pv(0, pa0, pa1);
+      pv(0, pa);
       __builtin_amdgcn_sched_barrier(0);
-      scores(1, s1);
+      scores_raw(skb, 1, s1, false);
       if (part) mask(1, s1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
-      pv(1, pb0, pb1);
+      for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[0][nt], s1[1][nt], pb[nt], l[nt]);
+      pv(1, pb);
       return;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // half 1's score MFMAs run while the VALU turns half 0's scores into
+    // step 1's score MFMAs run while the VALU turns step 0's scores into
     // weights (one region: the compiler interleaves them)
-    scores(1, s1);
+    scores_raw(skb, 1, s1, false);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[nt], pa0[nt], pa1[nt], l[nt]);
+    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[0][nt], s0[1][nt], pa[nt], l[nt]);
     __builtin_amdgcn_sched_barrier(0);
     if (part) mask(1, s1);
     __builtin_amdgcn_sched_barrier(0);
-    // half 0's PV MFMAs run while the VALU does half 1's weights (one region)
-    pv(0, pa0, pa1);
+    // step 0's PV MFMAs run while the VALU does step 1's weights (one region)
+    pv(0, pa);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[nt], pb0[nt], pb1[nt], l[nt]);
+    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[0][nt], s1[1][nt], pb[nt], l[nt]);
     __builtin_amdgcn_sched_barrier(0);
-    pv(1, pb0, pb1);
+    pv(1, pb);
   };
   auto pass = [&](bool preset) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x16{};
+      for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x4{};
       l[nt] = 0.0f;
     }
     cursor_reset();
@@ -558,7 +558,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   // with that shift, where every weight is <= 1 and the max itself weighs 1.
   __shared__ int redo;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) shift[nt] = f32x16{};
+  for (int nt = 0; nt < NT; ++nt) shift[nt] = f32x4{};
   // At most two passes, one copy of the pass code: the second pass runs only
   // when the first one's row sums left [1, 2^60].
   bool preset = false;
@@ -568,7 +568,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     if (preset) break;
     bool bad = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bad |= !(pair_sum(l[nt]) <= kOverflow);
+    for (int nt = 0; nt < NT; ++nt) bad |= !(quad_sum(l[nt]) <= kOverflow);
     __syncthreads();
     if (wave_any(bad) && lane == 0) redo = 1;  // every writer stores 1
     __syncthreads();
@@ -576,35 +576,31 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     float mx[NT];
     row_max(mx);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) shift[nt][j] = -mx[nt];
+    for (int nt = 0; nt < NT; ++nt) shift[nt] = f32x4{-mx[nt], -mx[nt], -mx[nt], -mx[nt]};
     preset = true;
   }
 
-  // ---- normalise and store: lane (query, g) holds dims 32dt + 8*j4 + 4g .. +4
+  // ---- normalise and store: lane (query l16, group g4) holds dims 16dt + 4g4 .. +4
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float inv = 1.0f / pair_sum(l[nt]);
+    const float inv = 1.0f / quad_sum(l[nt]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 v;
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        f32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = o[dt][nt][4 * j4 + i] * inv;
-        const bf16x4 h = __builtin_convertvector(v, bf16x4);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), ro,
-                                              qoff[nt] + (32 * dt + 8 * j4 + 4 * g) * 2, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) v[i] = o[dt][nt][i] * inv;
+      const bf16x4 hv = __builtin_convertvector(v, bf16x4);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), ro, qoff[nt] + (16 * dt + 4 * g4) * 2, 0,
+                                            0);
+    }
   }
 }
 
 }  // namespace
 
 int attn_bf16_block_m(int head_dim, bool small) {
-  if (head_dim == 64) return small ? 32 * Cfg<64, true>::WAVES * Cfg<64, true>::NT : 32 * Cfg<64, false>::WAVES * Cfg<64, false>::NT;
-  if (head_dim == 128) return small ? 32 * Cfg<128, true>::WAVES * Cfg<128, true>::NT : 32 * Cfg<128, false>::WAVES * Cfg<128, false>::NT;
+  if (head_dim == 64) return small ? 16 * Cfg<64, true>::WAVES * Cfg<64, true>::NT : 16 * Cfg<64, false>::WAVES * Cfg<64, false>::NT;
+  if (head_dim == 128) return small ? 16 * Cfg<128, true>::WAVES * Cfg<128, true>::NT : 16 * Cfg<128, false>::WAVES * Cfg<128, false>::NT;
   return 0;
 }
 
