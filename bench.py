@@ -17,7 +17,7 @@ The JSON line carries:
   cpu_baseline -- the fp64 oracle timed on a bounded sample of the same
                workload on this host's cores (rank 0, N=1 only).
   roofline.measured_mfma_ceiling -- after the timed steps, a dense
-               v_mfma_f32_32x32x16_bf16 stream on random and on constant
+               v_mfma_f32_16x16x32_bf16 stream (the kernel's instruction) on random and on constant
                operands: what this GPU sustains under its clock and power
                management (the published peak assumes 2.4 GHz throughout).
 """

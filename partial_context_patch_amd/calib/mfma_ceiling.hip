@@ -1,7 +1,7 @@
 // Dense bf16 MFMA throughput this GPU sustains, with random and with constant
-// operands: the practical ceiling of v_mfma_f32_32x32x16_bf16 (the attention
+// operands: the practical ceiling of v_mfma_f32_16x16x32_bf16 (the attention
 // kernel's instruction) under the board's clock and power management, which
-// depends on the data's switching activity.  Every wave runs four independent
+// depends on the data's switching activity.  Every wave runs eight independent
 // accumulator chains; operands cycle through eight register sets per lane.
 // Prints one JSON line.  A measurement utility, not part of the library.
 #include <hip/hip_runtime.h>
@@ -11,7 +11,7 @@
 #include <vector>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define CK(x)                                                                \
   do {                                                                       \
@@ -41,19 +41,19 @@ __global__ __launch_bounds__(256) void mfma_stream(const bf16x8* __restrict__ sr
       b[i] = b[0];
     }
   }
-  f32x16 c[4] = {};
+  f32x4 c[8] = {};
   const long long t0 = clock64(), w0 = wall_clock64();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(u + i) & 7], b[(u + 3 * i) & 7], c[i], 0, 0, 0);
+      for (int i = 0; i < 8; ++i)
+        c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(u + i) & 7], b[(u + 3 * i) & 7], c[i], 0, 0, 0);
   }
   const long long t1 = clock64(), w1 = wall_clock64();
   float s = 0.0f;
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 16; ++j) s += c[i][j];
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) s += c[i][j];
   out[blockIdx.x * 256 + threadIdx.x] = s;
   if (threadIdx.x == 0) {
     clk[blockIdx.x * 2] = t1 - t0;
@@ -103,10 +103,11 @@ int main() {
     long long hc[2];
     CK(hipMemcpy(hc, c, sizeof hc, hipMemcpyDeviceToHost));
     ghz[mode] = (double)hc[0] / (double)hc[1] * 0.1;  // wall_clock64 ticks at 100 MHz
-    const double mfmas = (double)blocks * 4 * iters * 8 * 4;
-    tf[mode] = mfmas * 32768.0 / (ms * 1e-3) / 1e12;
+    const double mfmas = (double)blocks * 4 * iters * 8 * 8;
+    tf[mode] = mfmas * 16384.0 / (ms * 1e-3) / 1e12;
   }
-  printf("{\"random_tflops\": %.1f, \"random_clock_ghz\": %.3f, \"constant_tflops\": %.1f, \"constant_clock_ghz\": %.3f}\n",
+  printf("{\"instruction\": \"v_mfma_f32_16x16x32_bf16\", \"random_tflops\": %.1f, \"random_clock_ghz\": %.3f, "
+         "\"constant_tflops\": %.1f, \"constant_clock_ghz\": %.3f}\n",
          tf[0], ghz[0], tf[1], ghz[1]);
   return 0;
 }
