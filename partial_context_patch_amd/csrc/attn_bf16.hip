@@ -127,11 +127,21 @@ __device__ __forceinline__ float max4(const f32x4& a) { return fmaxf(fmaxf(a[0],
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// 16-byte chunk permutation of LDS row r.  With it, each 8 lanes of a
-// ds_read_b128 (K fragments: rows {0..3, 8..11} + 16j + 4h, one chunk) and
-// the 16 lanes of each ds_read_b64_tr_b16 quarter (V fragments: 4 consecutive
-// rows x 2 adjacent chunks) hit 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+// 16-byte chunk permutation of LDS row r (16 slots of 16 bytes span the 64
+// banks).  The reads it serves:
+//   K fragments, ds_read_b128: each 8 lanes read one chunk of rows
+//     {0..3, 8..11} (+ 4h + 16j);
+//   V^T fragments, ds_read_b64_tr_b16: each 32 lanes read two adjacent
+//     chunks of rows {0..3, 8..11} (+ 32s + 16j).
+// d = 64 (two rows per 256 bytes): within each row parity the rows 0..3,
+// 8..11 get XOR masks {0, 4, 2, 6}, all differing above bit 0, so both
+// patterns hit distinct slots.  d = 128 (one row per 256 bytes): the eight
+// rows get eight masks that differ above bit 0.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 64) return ((r & 3) << 1) ^ (((r >> 3) & 1) << 1);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
@@ -289,7 +299,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     const int pos = (wave * CH + r) * 64 + lane;  // chunk slot in the tile
     const int row = pos / CPR, slot = pos % CPR;
     krow_c[r] = row;
-    lane_off[r] = (uint32_t)row * sn2 + (uint32_t)((slot ^ swz(row)) * 16);
+    lane_off[r] = (uint32_t)row * sn2 + (uint32_t)((slot ^ swz<D>(row)) * 16);
   }
   // Window mode: run 0 is the window (rows of cur_len keys, pitch apart) or,
   // in the text tile, every stored token; run 1 is the text tokens.  A run
@@ -391,7 +401,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int row = 32 * s + krow0 + 4 * h;
-        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((4 * ks + g4) ^ swz(row)) * 8)];
+        const bf16x8 kf = *(const bf16x8*)&skb[row * LDR + (((4 * ks + g4) ^ swz<D>(row)) * 8)];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           sc[h][nt] = mfma16(kf, qf[nt][ks], ks == 0 ? (raw ? f32x4{} : shift[nt]) : sc[h][nt]);
@@ -484,8 +494,8 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
       for (int dt = 0; dt < DT; ++dt) {
         const int r0 = 32 * s + vrow, r1 = r0 + 4;
         const int col = 16 * dt + vcol;  // multiple of 4: one 8-byte half of a chunk
-        const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz(r0)) * 8) + (col & 7)];
-        const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz(r1)) * 8) + (col & 7)];
+        const __bf16* p0p = &svb[r0 * LDR + (((col >> 3) ^ swz<D>(r0)) * 8) + (col & 7)];
+        const __bf16* p1p = &svb[r1 * LDR + (((col >> 3) ^ swz<D>(r1)) * 8) + (col & 7)];
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p0p);
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1p);
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
