@@ -71,8 +71,11 @@ typedef enum { NPA_MODE_STRIPS = 0, NPA_MODE_WINDOW = 1 } npa_mode_t;
  * with tokens row-major over the map, t = r*map_w + c (after the halo's
  * text_tokens, when there are any: t = text_tokens + r*map_w + c).  Every
  * pointer must be 16-byte aligned and stride_b/stride_n/stride_h must keep
- * each head's row 16-byte aligned.  Limits: text_tokens + map_h*map_w <= 2^24,
- * batch*heads*tiles*blocks < 2^31.  batch and heads may be 0: such a call is
+ * each head's row 16-byte aligned.  Distinct (b, t, j, e) must address
+ * distinct elements (checked: ordered by stride, each dimension with more than
+ * one index must step past the span of the ones inside it; otherwise
+ * NPA_ERR_INVALID_ARG -- out would race).  Limits: text_tokens + map_h*map_w
+ * <= 2^24, batch*heads*tiles*blocks < 2^31.  batch and heads may be 0: such a call is
  * validated, computes nothing, touches no memory and returns NPA_OK (its
  * pointers may then be NULL); head_dim, map_h, map_w are >= 1. */
 typedef struct {
@@ -148,8 +151,9 @@ int64_t npa_useful_flops(const npa_layout_t* layout, const npa_halo_t* halo);
  * x, ref, out: fp32 device tensors [n, c, h, w] contiguous, 16-byte aligned;
  * out must not alias x or ref (the stencil reads neighbours).  sigma in
  * (0, 8]; h, w >= 1; n, c >= 0 (n*c = 0: nothing to do, NPA_OK, pointers
- * unchecked).  With w_t = 1 this is also latent frequency mixing:
- * low frequencies of ref, high frequencies of x. */
+ * unchecked); n*c <= 65535 and n*c*h*w <= 2^40 (else NPA_ERR_SHAPE).
+ * With w_t = 1 this is also latent frequency mixing: low frequencies of ref,
+ * high frequencies of x. */
 npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t n,
                           int32_t c, int32_t h, int32_t w, float w_t, float sigma,
                           void* hip_stream);
@@ -159,7 +163,9 @@ npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t 
  *   out = eps + w_t * mask * (eps_ref_prev - eps)        element-wise,
  * where eps_ref_prev is the reference patch's prediction from the previous
  * step and mask the normalised cross-attention mask (caller-supplied).
- * fp32 device arrays of `count` elements, 16-byte aligned; out may alias eps. */
+ * fp32 device arrays of `count` elements (0 <= count <= 2^40), 16-byte
+ * aligned; out may be any of the inputs itself (the update is element-wise),
+ * while a shifted overlap with an input is NPA_ERR_INVALID_ARG. */
 npa_status_t npa_asg_blend(const float* eps, const float* eps_ref_prev, const float* mask,
                            float* out, int64_t count, float w_t, void* hip_stream);
 

@@ -147,6 +147,33 @@ void extent(const void* p, const npa_layout_t* L, int64_t N, int64_t esize, uint
   *hi = *lo + (uintptr_t)(last * esize);
 }
 
+// Do distinct (batch, token, head, channel) indices address distinct elements?
+// Tested the sufficient way: taken in order of increasing stride, every
+// dimension with more than one index steps past the whole span of the
+// dimensions inside it (the channels are the contiguous innermost run).
+// Returns false also when the span does not fit in 2^62 elements.
+bool one_to_one(const npa_layout_t* L, int64_t tokens) {
+  struct Dim {
+    int64_t stride, n;
+  } d[3] = {{L->stride_b, L->batch}, {L->stride_n, tokens}, {L->stride_h, L->heads}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (d[j].stride < d[i].stride) {
+        const Dim t = d[i];
+        d[i] = d[j];
+        d[j] = t;
+      }
+  const int64_t limit = int64_t(1) << 62;
+  int64_t span = L->head_dim;
+  for (const Dim& x : d) {
+    if (x.n <= 1) continue;
+    if (x.stride < span) return false;
+    if (x.stride > (limit - span) / (x.n - 1)) return false;
+    span += x.stride * (x.n - 1);
+  }
+  return true;
+}
+
 bool overlaps(const void* a, const void* b, const npa_layout_t* L, int64_t N, int64_t esize) {
   if (!a || !b) return false;
   uintptr_t a0, a1, b0, b1;
@@ -229,9 +256,10 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
       L->stride_h % vec)
     return fail(NPA_ERR_INVALID_ARG, "strides must be >= 0 and multiples of %lld elements",
                 (long long)vec);
-  if (L->stride_n < (int64_t)L->heads * L->head_dim && L->stride_h < L->head_dim)
-    return fail(NPA_ERR_INVALID_ARG, "strides overlap heads");
   const int64_t tokens = (int64_t)g.T + (int64_t)L->map_h * L->map_w;  // stored per (batch, head)
+  if (!one_to_one(L, tokens))
+    return fail(NPA_ERR_INVALID_ARG,
+                "the strides map two (batch, token, head) rows onto overlapping memory (the output would race)");
   for (const void* p : ins)
     if (overlaps(out, p, L, tokens, esize)) return fail(NPA_ERR_INVALID_ARG, "out must not alias an input");
 
@@ -302,6 +330,8 @@ npa_status_t npa_sg_blend(const float* x, const float* ref, float* out, int32_t 
     return fail(NPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const int64_t planes = (int64_t)n * c;
   if (planes > 65535) return fail(NPA_ERR_SHAPE, "n*c=%lld exceeds 65535 planes", (long long)planes);
+  if ((int64_t)h * w > (int64_t(1) << 40) / planes)
+    return fail(NPA_ERR_SHAPE, "n*c*h*w exceeds 2^40 elements");
   const uintptr_t bytes = (uintptr_t)planes * h * w * sizeof(float);
   const uintptr_t o0 = (uintptr_t)out, x0 = (uintptr_t)x, r0 = (uintptr_t)ref;
   if ((o0 < x0 + bytes && x0 < o0 + bytes) || (o0 < r0 + bytes && r0 < o0 + bytes))
@@ -334,7 +364,16 @@ npa_status_t npa_asg_blend(const float* eps, const float* eps_ref_prev, const fl
   if (!aligned16(eps) || !aligned16(eps_ref_prev) || !aligned16(mask) || !aligned16(out))
     return fail(NPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (count < 0) return fail(NPA_ERR_SHAPE, "count must be >= 0");
+  if (count > (int64_t(1) << 40)) return fail(NPA_ERR_SHAPE, "count exceeds 2^40 elements");
   if (!std::isfinite(w_t)) return fail(NPA_ERR_INVALID_ARG, "w_t must be finite");
+  // element-wise: out may be any input itself, but a shifted overlap would
+  // let one element's result feed another element's inputs
+  const uintptr_t bytes = (uintptr_t)count * sizeof(float), o0 = (uintptr_t)out;
+  for (const float* p : {eps, eps_ref_prev, mask}) {
+    const uintptr_t p0 = (uintptr_t)p;
+    if (p0 != o0 && o0 < p0 + bytes && p0 < o0 + bytes)
+      return fail(NPA_ERR_INVALID_ARG, "out must be an input itself or not overlap it");
+  }
   if (count == 0) return ok();
   const hipError_t e = npa::launch_asg_blend(eps, eps_ref_prev, mask, out, count, w_t,
                                              reinterpret_cast<hipStream_t>(hip_stream));

@@ -186,6 +186,55 @@ def test_validation_errors(lib):
     assert lib.npa_sg_blend(0, 2 << 20, 3 << 20, 1, 4, 8, 8, 0.5, 4.0, None) == npa.NPA_ERR_INVALID_ARG
     assert lib.npa_asg_blend(1 << 20, 2 << 20, 3 << 20, 4 << 20, -1, 0.5, None) == npa.NPA_ERR_SHAPE
     assert lib.npa_asg_blend(1 << 20, 2 << 20, 3 << 20, 4 << 20, 0, 0.5, None) == npa.NPA_OK
+    assert lib.npa_sg_blend(1 << 20, 2 << 20, 3 << 20, 1, 1, 1 << 30, 1 << 11, 0.5, 4.0, None) == npa.NPA_ERR_SHAPE
+
+
+def test_layouts_that_map_rows_onto_each_other_are_refused(lib):
+    """Q, K, V and out share one layout; one where two (batch, token, head)
+    rows overlap would make the output race, so it is refused on the host."""
+    strips = npa.make_halo(strips=4, p=0.3)
+    N, Hh, d = 32 * 32, 2, 64
+    fine = [
+        (N * Hh * d, Hh * d, d),                  # [B, N, H, D]
+        (N * Hh * d, d, N * d),                   # [B, H, N, D]
+        (N * (Hh * d + 8) + 64, Hh * d + 8, d + 8),  # padded rows
+        (d, 2 * Hh * d, 2 * d),                   # batch innermost, interleaved
+    ]
+    for st in fine:
+        L = npa.make_layout(2, Hh, d, 32, 32, strides=st)
+        # passes the layout check; stops later, at the aliasing check of
+        # these fake pointers (the extents overlap)
+        _status(lib, L, strips, q=1 << 30, k=2 << 30, v=3 << 30, ks=4 << 30, vs=5 << 30, out=6 << 30)
+        assert b"overlapping memory" not in lib.npa_last_error(), st
+    bad = [
+        (0, Hh * d, d),                           # batches on top of each other
+        (N * Hh * d, Hh * d, 0),                  # heads on top of each other
+        (N * Hh * d, 8, d),                       # tokens overlap
+        (N * Hh * d, Hh * d, 32),                 # heads half overlap
+        (Hh * d, Hh * d, d),                      # batch stride equals the token stride
+    ]
+    for st in bad:
+        L = npa.make_layout(2, Hh, d, 32, 32, strides=st)
+        assert _status(lib, L, strips) == npa.NPA_ERR_INVALID_ARG, st
+        assert b"overlapping memory" in lib.npa_last_error(), st
+    # a dimension of one index may have any stride
+    L = npa.make_layout(1, 1, d, 32, 32, strides=(0, d, 0))
+    _status(lib, L, strips)
+    assert b"overlapping memory" not in lib.npa_last_error()
+
+
+def test_asg_out_is_an_input_or_apart(lib):
+    """The element-wise ASG update may write over an input, but not over a
+    shifted copy of one."""
+    n = 1024
+    base = 1 << 30
+    eps, ref, mask, out = base, base + (1 << 20), base + (2 << 20), base + (3 << 20)
+    for o in (eps, ref, mask):
+        assert lib.npa_asg_blend(eps, ref, mask, o, 0, 0.5, None) == npa.NPA_OK
+    for o in (eps + 16, ref - 16, mask + 4 * n - 16):
+        assert lib.npa_asg_blend(eps, ref, mask, o, n, 0.5, None) == npa.NPA_ERR_INVALID_ARG
+        assert b"overlap" in lib.npa_last_error()
+    assert lib.npa_asg_blend(eps, ref, mask, out, 1 << 41, 0.5, None) == npa.NPA_ERR_SHAPE
 
 
 def test_empty_calls_are_validated_no_ops(lib):
