@@ -221,23 +221,35 @@ def main() -> int:
     # structure-guidance blend: reads x and ref, writes out, 4 bytes each per element
     sg_bytes = 12 * sgw["channels"] * sgw["map_h"] * sgw["map_w"]
 
-    # The blend is an ~8 us kernel, and an event pair around each launch adds ~2 us
-    # to it, so it is also timed as back-to-back launches between two events.  An
-    # elementwise op that moves the same bytes (x + ref: reads both, writes one
-    # array) gives the streaming floor of a launch of this size.
-    def loop_ms(fn, n=100):
-        for _ in range(10):
-            fn()
+    # The blend is an ~8 us kernel: an event pair around each launch adds ~2 us to
+    # it, and a Python loop of launches cannot issue them that fast.  So it is
+    # also timed as 100 launches captured in one HIP graph, replayed between two
+    # events.  An elementwise op that moves the same bytes (x + ref: reads both,
+    # writes one array), timed the same way, gives the streaming floor of a
+    # launch of this size.
+    def graph_ms(fn, n=100):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(n):
-            fn()
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    sg_loop = loop_ms(lambda: npa.sg_blend(x, ref, sgw["w_t"], sgw["sigma"], out=sg_out))
-    floor_ms = loop_ms(lambda: torch.add(x, ref, out=sg_out))
+    sg_loop = graph_ms(lambda: npa.sg_blend(x, ref, sgw["w_t"], sgw["sigma"], out=sg_out))
+    floor_ms = graph_ms(lambda: torch.add(x, ref, out=sg_out))
     traffic = profiling.load_traffic(name)
     sclk = clock.get("sclk_mhz")
 

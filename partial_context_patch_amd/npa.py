@@ -185,7 +185,7 @@ def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], st
     if dt is None:
         raise TypeError("q must be bfloat16 or float32")
     if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     ts = [t for t in (q, k, v, k_stale, v_stale, out) if t is not None]
     for t in ts:
         if not t.is_cuda or t.device != q.device:
@@ -197,8 +197,10 @@ def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], st
     L = make_layout(B, Hh, d, H, W, dtype=dt, strides=q.stride()[:3], scale=scale)
     h = make_halo(strips=strips, p=p, halo_rows=halo_rows, tile=tile, halo=halo, text_tokens=text_tokens)
     ptr = lambda t: None if t is None else t.data_ptr()
-    _check(lib.npa_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(k_stale), ptr(v_stale), ctypes.byref(L), ctypes.byref(h),
-                            ptr(out), _stream_ptr(q.device)))
+    # the library launches on the current device, on that device's current stream
+    with torch.cuda.device(q.device):
+        _check(lib.npa_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(k_stale), ptr(v_stale), ctypes.byref(L),
+                                ctypes.byref(h), ptr(out), _stream_ptr(q.device)))
     return out
 
 
@@ -212,11 +214,14 @@ def sg_blend(x, ref, w_t: float, sigma: float, out=None):
     if out is None:
         out = torch.empty_like(x)
     for t in (x, ref, out):
-        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("x, ref, out must be contiguous fp32 GPU tensors")
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda or t.device != x.device:
+            raise ValueError("x, ref, out must be contiguous fp32 tensors on one GPU")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
     n, c, h, w = x.shape
-    _check(lib.npa_sg_blend(x.data_ptr(), ref.data_ptr(), out.data_ptr(), n, c, h, w, float(w_t), float(sigma),
-                            _stream_ptr(x.device)))
+    with torch.cuda.device(x.device):
+        _check(lib.npa_sg_blend(x.data_ptr(), ref.data_ptr(), out.data_ptr(), n, c, h, w, float(w_t), float(sigma),
+                                _stream_ptr(x.device)))
     return out
 
 
@@ -228,8 +233,10 @@ def asg_blend(eps, eps_ref_prev, mask, w_t: float, out=None):
     if out is None:
         out = torch.empty_like(eps)
     for t in (eps, eps_ref_prev, mask, out):
-        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda or t.shape != eps.shape:
-            raise ValueError("eps, eps_ref_prev, mask, out must be contiguous fp32 GPU tensors of one shape")
-    _check(lib.npa_asg_blend(eps.data_ptr(), eps_ref_prev.data_ptr(), mask.data_ptr(), out.data_ptr(), eps.numel(),
-                             float(w_t), _stream_ptr(eps.device)))
+        if (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda or t.shape != eps.shape
+                or t.device != eps.device):
+            raise ValueError("eps, eps_ref_prev, mask, out must be contiguous fp32 tensors of one shape on one GPU")
+    with torch.cuda.device(eps.device):
+        _check(lib.npa_asg_blend(eps.data_ptr(), eps_ref_prev.data_ptr(), mask.data_ptr(), out.data_ptr(),
+                                 eps.numel(), float(w_t), _stream_ptr(eps.device)))
     return out

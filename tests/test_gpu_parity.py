@@ -458,6 +458,33 @@ def test_regular_shape_full_compare(H, W, B, Hh, d, spec):
     assert np.abs(got - ref).max() <= ATOL["bf16"]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_strided_views_match_contiguous_bit_for_bit(dt):
+    """Inputs that are views into padded, heads-outer buffers, and out=None:
+    the output is allocated with q's strides, and every row equals the
+    contiguous call's bit for bit (a row's arithmetic does not depend on where
+    its neighbours are stored)."""
+    H = W = 24
+    B, Hh, d = 2, 3, 64
+    spec = A.Strips(4, p=0.3)
+    inp = WL.attention_inputs(B, Hh, d, H, W, seed=5, dtype=dt)
+    want = _run(inp, H, W, spec, dt)
+
+    def view(a):
+        t = _dev(a, dt)  # [B, N, Hh, d] contiguous
+        buf = torch.full((B, Hh, H * W, d + 8), float("nan"), device="cuda", dtype=TDT[dt])
+        buf[..., :d] = t.permute(0, 2, 1, 3)
+        return buf[..., :d].permute(0, 2, 1, 3)  # strides (Hh*N*(d+8), d+8, N*(d+8), 1)
+
+    q, k, v, ks, vs = (view(inp[n]) for n in ("q", "k", "v", "k_stale", "v_stale"))
+    assert q.stride() == (Hh * H * W * (d + 8), d + 8, H * W * (d + 8), 1)
+    out = npa.attn_fwd(q, k, v, ks, vs, map_hw=(H, W), **_kw(spec))
+    torch.cuda.synchronize()
+    assert out.stride() == q.stride()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)
+
+
 def test_calls_replay_from_a_hip_graph():
     """npa_attn_fwd and npa_sg_blend captured into one HIP graph: every replay
     (with eager work and synchronisations between replays) reproduces the
