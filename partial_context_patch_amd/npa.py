@@ -7,8 +7,8 @@ there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
-import math
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_void_p
 from typing import Optional, Sequence, Tuple
@@ -163,6 +163,16 @@ def _stream_ptr(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on(device):
+    """Make `device` current for the call (the library launches on the current
+    device); a no-op context when it already is, which is the common case."""
+    import torch
+
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], strips: Optional[int] = None,
              p: Optional[float] = None, halo_rows: Optional[int] = None, tile: Optional[Tuple[int, int]] = None,
              halo: Optional[Tuple[int, int]] = None, text_tokens: int = 0, scale: Optional[float] = None, out=None):
@@ -198,7 +208,7 @@ def attn_fwd(q, k, v, k_stale=None, v_stale=None, *, map_hw: Tuple[int, int], st
     h = make_halo(strips=strips, p=p, halo_rows=halo_rows, tile=tile, halo=halo, text_tokens=text_tokens)
     ptr = lambda t: None if t is None else t.data_ptr()
     # the library launches on the current device, on that device's current stream
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         _check(lib.npa_attn_fwd(ptr(q), ptr(k), ptr(v), ptr(k_stale), ptr(v_stale), ctypes.byref(L),
                                 ctypes.byref(h), ptr(out), _stream_ptr(q.device)))
     return out
@@ -219,7 +229,7 @@ def sg_blend(x, ref, w_t: float, sigma: float, out=None):
     if out.shape != x.shape:
         raise ValueError("out must have x's shape")
     n, c, h, w = x.shape
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         _check(lib.npa_sg_blend(x.data_ptr(), ref.data_ptr(), out.data_ptr(), n, c, h, w, float(w_t), float(sigma),
                                 _stream_ptr(x.device)))
     return out
@@ -236,7 +246,7 @@ def asg_blend(eps, eps_ref_prev, mask, w_t: float, out=None):
         if (t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda or t.shape != eps.shape
                 or t.device != eps.device):
             raise ValueError("eps, eps_ref_prev, mask, out must be contiguous fp32 tensors of one shape on one GPU")
-    with torch.cuda.device(eps.device):
+    with _on(eps.device):
         _check(lib.npa_asg_blend(eps.data_ptr(), eps_ref_prev.data_ptr(), mask.data_ptr(), out.data_ptr(),
                                  eps.numel(), float(w_t), _stream_ptr(eps.device)))
     return out
