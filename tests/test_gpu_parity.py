@@ -130,6 +130,32 @@ def test_workload_full_size_sampled(name):
         assert err <= ATOL[w["dtype"]], f"{name} (b={b}, head={j}): max abs err {err}"
 
 
+@pytest.mark.parametrize("name", ["sdxl2048_strips", "flux4096_npa", "sdxl1024_strips"])
+def test_repeated_calls_are_bitwise_identical(name):
+    """The kernels use no atomics and no order-dependent reduction across
+    workgroups, so the same call gives the same bits every time; a race on the
+    double-buffered K/V tiles or on the copy cursor would show up here as
+    run-to-run differences.  Five back-to-back calls at full size, with other
+    work (a different call) interleaved between them."""
+    w = WL.ATTENTION_WORKLOADS[name]
+    print(f"[parity] repeatability {name}", flush=True)
+    inp = WL.workload_inputs(name)
+    dt = TDT[w["dtype"]]
+    t = {n: (None if a is None else _dev(a, w["dtype"])) for n, a in inp.items()}
+    kw = WL.halo_kwargs(w)
+    hw = (w["map_h"], w["map_w"])
+    first = npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], map_hw=hw, **kw)
+    other = torch.empty_like(first)
+    for rep in range(4):
+        # a different call in between: the swapped roles of q and k
+        npa.attn_fwd(t["k"], t["q"], t["v"], t["k_stale"], t["v_stale"], map_hw=hw, out=other, **kw)
+        again = torch.full_like(first, float("nan"))
+        npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], map_hw=hw, out=again, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           first.view(torch.int16 if dt == torch.bfloat16 else torch.int32)), f"{name}: repeat {rep}"
+
+
 # ----------------------------------------------------------- structural
 @pytest.mark.parametrize("spec", [A.Strips(2, halo_rows=1), A.Strips(4, halo_rows=2), A.Strips(4, halo_rows=0),
                                   A.Windows(2, 2, 1, 1), A.Windows(1, 4, 2, 0)])
