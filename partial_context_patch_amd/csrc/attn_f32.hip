@@ -1,14 +1,35 @@
-// Partial-context patch attention, fp32 throughout (no bf16 rounding anywhere).
+// Partial-context patch attention, fp32 throughout (no bf16 rounding anywhere),
+// on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).
 //
 // Same partial key sets as the bf16 kernel (own strip fresh plus stale halo
 // rows, "Partially Conditioned Patch Parallelism ...", "What carries the
-// argument"; or a clipped window, "ScaleDiff ...", "Approach").  Each query is
-// served by kSplit consecutive lanes: K/V blocks are staged in LDS, lane s of a
-// query takes the block's keys s, s + kSplit, ..., keeps its own running max,
-// sum and output (blockwise online softmax with expf), and the lanes' partial
-// results are merged once at the end by cross-lane exchange.  This is the
-// accuracy path (fp32 inputs), not the throughput path; the key split keeps
-// small fp32 calls from running on a handful of serial threads.
+// argument"; or a clipped window, "ScaleDiff ...", "Approach").
+//
+// Workgroup = 4 waves, one 16-query tile per wave (64 queries), sharing each
+// K/V block (64 keys; 32 at d = 128) staged in LDS; the next block's global
+// loads are in flight in registers while the current one is computed.  Per
+// block and wave:
+//
+//   S^T = K Q^T   one 16-key x 16-query tile per 16 keys.  The instruction
+//                 takes A[m][k] from lane (m + 16k), B[k][n] from lane
+//                 (n + 16k) and leaves D[4g + i][n] in entry i of lane
+//                 (n + 16g).  Lane group
+//                 g supplies the contiguous quarter d in [g*D/4, (g+1)*D/4) of
+//                 the dot product, so its K reads are 16-byte row reads and its
+//                 Q quarter stays in registers.  Lane (n + 16g) ends with the
+//                 scores of keys 4g..4g+3 of each tile for query n.
+//   softmax       exact block max (in-lane, then across the four lane groups),
+//                 running max / sum with one rescale of O per block, exp2 of
+//                 scores pre-scaled by scale*log2(e) (folded into Q).
+//   O^T += V^T P^T  MFMA (tile t, j) contracts keys 16t + 4g + j (g = the lane
+//                 group), so the B operand is the lane's own weight of entry j
+//                 -- the score layout feeds PV with no data movement.  Output
+//                 row m of 16-dim step dt is channel m*DT + dt: a lane's V
+//                 operands for all steps are DT consecutive floats of one key
+//                 row, and at the end a lane holds 4*DT consecutive channels
+//                 of its query's output row.
+//
+// This is the accuracy path for fp32 inputs; products and sums stay in fp32.
 #include <hip/hip_runtime.h>
 
 #include "npa_internal.hpp"
@@ -16,11 +37,12 @@
 namespace npa {
 namespace {
 
-constexpr int kThreads = 256;                // threads per workgroup
-constexpr int kSplit = 16;                   // lanes per query
-constexpr int kQueries = kThreads / kSplit;  // queries per workgroup
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;  // threads per workgroup
+constexpr int kQueries = 16 * kWaves;  // queries per workgroup (one 16-query tile per wave)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int MODE>
 __device__ __forceinline__ int token_of(const Run& r, int j) {
@@ -29,122 +51,176 @@ __device__ __forceinline__ int token_of(const Run& r, int j) {
   return r.start + row * r.pitch + (j - row * r.row_len);
 }
 
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Token index and source buffer of key j (0 <= j < nk) of the tile's key runs.
+template <int MODE>
+__device__ __forceinline__ int key_token(const TileRuns& tr, int j, bool& stale) {
+  if (j < tr.nk[0]) {
+    stale = tr.src[0] != 0;
+    return token_of<MODE>(tr.k[0], j);
+  }
+  j -= tr.nk[0];
+  if (j < tr.nk[1]) {
+    stale = tr.src[1] != 0;
+    return token_of<MODE>(tr.k[1], j);
+  }
+  stale = tr.src[2] != 0;
+  return token_of<MODE>(tr.k[2], j - tr.nk[1]);
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
-  constexpr int BN = D <= 64 ? 64 : 32;  // keys per LDS block: BN / kSplit per lane
-  constexpr int C4 = D / 4;   // float4 chunks per key row
-  constexpr int LD = D + 4;   // LDS row pitch: the kSplit lanes of a query read
-                              // kSplit consecutive rows, 16 bytes apart in bank order
-  __shared__ __attribute__((aligned(16))) float sk[BN * LD];
-  __shared__ __attribute__((aligned(16))) float sv[BN * LD];
+  constexpr int kBN = D == 128 ? 32 : 64;  // keys per LDS block
+  constexpr int NTL = kBN / 16;            // 16-key tiles per block
+  constexpr int LD = D + 4;                // LDS row pitch (floats)
+  constexpr int C4 = D / 4;                // 16-byte chunks per key row
+  constexpr int CH = kBN * C4 / kThreads;  // chunks per thread per K (and V) block
+  constexpr int DQ = D / 4;                // channels per lane group in S^T
+  constexpr int DT = D / 16;               // 16-dim steps of O^T
+  static_assert(CH * kThreads == kBN * C4 && DT >= 2 && DT % 2 == 0, "shape");
+  __shared__ __attribute__((aligned(16))) float sk[kBN * LD];
+  __shared__ __attribute__((aligned(16))) float sv[kBN * LD];
 
-  const int tid = threadIdx.x, sub = tid % kSplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
   const BlockCoord bc = decode_block(a, blockIdx.x, false);
-  const int qb = bc.qb, tile = bc.tile, head = bc.head, b = bc.b;
-
-  const TileRuns tr = tile_runs(a.g, tile);
+  const TileRuns tr = tile_runs(a.g, bc.tile);
   const int nq = tr.q.count();
   const int nk = tr.nk[0] + tr.nk[1] + tr.nk[2];
-  const int64_t bh = (int64_t)b * a.sb + (int64_t)head * a.sh;
-  const float* qp = (const float*)a.q;
+  const int64_t bh = (int64_t)bc.b * a.sb + (int64_t)bc.head * a.sh;
 
-  const int qi = qb * kQueries + tid / kSplit;
+  // this lane's query (column l16 of the wave's tile) and its quarter of Q,
+  // pre-scaled by scale * log2(e)
+  const int qi = bc.qb * kQueries + wave * 16 + l16;
   const bool ok = qi < nq;
   const int64_t qoff = bh + (int64_t)(ok ? token_of<MODE>(tr.q, qi) : 0) * a.sn;
-
-  float q[D], o[D];
+  float qf[DQ];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    q[e] = ok ? qp[qoff + e] * a.scale : 0.0f;
-    o[e] = 0.0f;
+  for (int e = 0; e < DQ; e += 4) {
+    const f32x4 v = ok ? *(const f32x4*)((const float*)a.q + qoff + g4 * DQ + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[e + i] = v[i] * a.c;
   }
-  float m = -INFINITY, l = 0.0f;
 
-  for (int k0 = 0; k0 < nk; k0 += BN) {
-    __syncthreads();
-    for (int c = tid; c < BN * C4; c += kThreads) {
-      const int key = c / C4, dc = c % C4;
-      int j = k0 + key;
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // running max of the query's scores (log2 domain)
+  float l = 0.0f;       // sum of this lane's weights (its keys 4g4..4g4+3 of every tile)
+
+  // K/V block staging: chunk c of this thread is key (tid + c*kThreads) / C4
+  f32x4 rk[CH], rv[CH];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * kThreads, key = idx / C4, dc = idx % C4;
+      const int j = k0 + key;
+      rk[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      rv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (j < nk) {
-        int run = 0;
-        if (j >= tr.nk[0]) {
-          j -= tr.nk[0];
-          run = 1;
-          if (j >= tr.nk[1]) {
-            j -= tr.nk[1];
-            run = 2;
-          }
-        }
-        const int64_t off = bh + (int64_t)token_of<MODE>(tr.k[run], j) * a.sn + dc * 4;
-        const float* kp = (const float*)(tr.src[run] ? a.ks : a.kf);
-        const float* vp = (const float*)(tr.src[run] ? a.vs : a.vf);
-        kk = *(const f32x4*)(kp + off);
-        vv = *(const f32x4*)(vp + off);
+        bool stale;
+        const int64_t off = bh + (int64_t)key_token<MODE>(tr, j, stale) * a.sn + dc * 4;
+        rk[c] = *(const f32x4*)((const float*)(stale ? a.ks : a.kf) + off);
+        rv[c] = *(const f32x4*)((const float*)(stale ? a.vs : a.vf) + off);
       }
-      *(f32x4*)&sk[key * LD + dc * 4] = kk;
-      *(f32x4*)&sv[key * LD + dc * 4] = vv;
     }
+  };
+  auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = tid + c * kThreads, key = idx / C4, dc = idx % C4;
+      *(f32x4*)&sk[key * LD + dc * 4] = rk[c];
+      *(f32x4*)&sv[key * LD + dc * 4] = rv[c];
+    }
+  };
+
+  load(0);
+  for (int k0 = 0; k0 < nk; k0 += kBN) {
+    __syncthreads();  // every wave is done with the previous block
+    store();
     __syncthreads();
-    const int nvalid = nk - k0 < BN ? nk - k0 : BN;
-    constexpr int KL = BN / kSplit;  // keys of the block this lane takes
-    float sc[KL];
-    float mb = -INFINITY;
+    if (k0 + kBN < nk) load(k0 + kBN);
+    const int nvalid = nk - k0 < kBN ? nk - k0 : kBN;
+
+    // S^T, the block's 16-key tiles interleaved (independent accumulation chains)
+    f32x4 s[NTL];
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int k = i * kSplit + sub;
-      // four independent partial sums shorten the dependent chain
-      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NTL; ++t) s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < D; ++e) acc[e & 3] = __builtin_fmaf(q[e], sk[k * LD + e], acc[e & 3]);
-      sc[i] = (k < nvalid) ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : -INFINITY;
-      mb = fmaxf(mb, sc[i]);
+    for (int e = 0; e < DQ; e += 4) {
+      f32x4 kv[NTL];
+#pragma unroll
+      for (int t = 0; t < NTL; ++t) kv[t] = *(const f32x4*)&sk[(16 * t + l16) * LD + g4 * DQ + e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) s[t] = mfma(kv[t][i], qf[e + i], s[t]);
     }
-    const float mn = fmaxf(m, mb);
-    if (mn == -INFINITY) continue;  // this lane has seen no key yet
-    if (mn > m) {  // rescale only when the running max rises
-      const float alpha = expf(m - mn);
-      l *= alpha;
+    // keys past the block's end (entry i of tile t is key 16t + 4*g4 + i)
+    if (nvalid < kBN) {
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] *= alpha;
+      for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * t + 4 * g4 + i >= nvalid) s[t][i] = -INFINITY;
     }
+    float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      const int k = i * kSplit + sub;
-      const float p = (k < nvalid) ? expf(sc[i] - mn) : 0.0f;
-      l += p;
+    for (int t = 0; t < NTL; ++t) mt = fmaxf(mt, fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    // no finite score yet (only for non-finite inputs): keep the zero state
+    const float sh = (mn == -INFINITY) ? 0.0f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - sh);
+    l *= alpha;
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] = __builtin_fmaf(p, sv[k * LD + e], o[e]);
-    }
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     m = mn;
+    float p[NTL][4];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[t][i] = __builtin_amdgcn_exp2f(s[t][i] - sh);
+        l += p[t][i];
+      }
+
+    // O^T += V^T P^T: MFMA (t, j) contracts keys 16t + 4*g4 + j
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float* vr = &sv[(16 * t + 4 * g4 + j) * LD + l16 * DT];
+        float vv[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; dt += 2) {
+          const f32x2 w = *(const f32x2*)(vr + dt);
+          vv[dt] = w[0];
+          vv[dt + 1] = w[1];
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = mfma(vv[dt], p[t][j], o[dt]);
+      }
   }
-  // merge the kSplit lanes of each query: common max, then weighted sums
-  float mq = m;
-#pragma unroll
-  for (int w = 1; w < kSplit; w <<= 1) mq = fmaxf(mq, __shfl_xor(mq, w));
-  const float f = (m == -INFINITY) ? 0.0f : expf(m - mq);
-  float lq = l * f;
-#pragma unroll
-  for (int w = 1; w < kSplit; w <<= 1) lq += __shfl_xor(lq, w);
-#pragma unroll
-  for (int e = 0; e < D; ++e) {
-    float v = o[e] * f;
-#pragma unroll
-    for (int w = 1; w < kSplit; w <<= 1) v += __shfl_xor(v, w);
-    o[e] = v;
-  }
+
+  // the query's keys are spread over the four lane groups
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
   if (!ok) return;
-  // every lane of the query holds the merged row; lane s stores its D/kSplit slice
-  float* op = (float*)a.o;
-  const float inv = 1.0f / lq;
-  constexpr int PER = D / kSplit;
+  const float inv = 1.0f / lt;
+  // entry i of o[dt] is channel (4*g4 + i)*DT + dt
+  float* op = (float*)a.o + qoff + 4 * g4 * DT;
 #pragma unroll
-  for (int e = 0; e < D; e += 4) {
-    if (e / PER == sub) {
-      f32x4 v = {o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv};
-      *(f32x4*)(op + qoff + e) = v;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int dt = 0; dt < DT; dt += 2) {
+      const f32x2 w = {o[dt][i] * inv, o[dt + 1][i] * inv};
+      *(f32x2*)(op + i * DT + dt) = w;
     }
-  }
 }
 
 template <int D>
