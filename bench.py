@@ -120,6 +120,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sdxl4096_npa")
+    ap.add_argument("--dtype", choices=("bf16", "f32"), default=None,
+                    help="run the workload's shape in this dtype instead of its own (f32: the fp32 path; "
+                         "bf16 head sizes are 64 and 128)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--settle", type=float, default=3.0,
                     help="seconds of back-to-back steps before the warm-up steps, so that the GPU's clock "
@@ -148,10 +151,12 @@ def main() -> int:
     npa.load(build_if_missing=False)
     name = args.workload
     w = WL.ATTENTION_WORKLOADS[name]
+    if args.dtype is not None:
+        w = dict(w, dtype=args.dtype)
     sgw = WL.SG_WORKLOAD
     dev = torch.device("cuda:0")
-    log(f"workload {name}: {w['what']}")
-    inp = WL.workload_inputs(name)
+    log(f"workload {name} ({w['dtype']}): {w['what']}")
+    inp = WL.attention_inputs(**w, stale=(w["mode"] == "strips"))
     tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     t = {n: (None if a is None else torch.from_numpy(a).to(dev).to(tdt)) for n, a in inp.items()}
     out = torch.empty_like(t["q"])

@@ -85,17 +85,21 @@ def counters(pmc_dirs, workload: str, cmd: str) -> str:
             for r in csv.DictReader(open(f)):
                 per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
     copy = next((k for k in per if "copyBuffer" in k), None)
-    attn = next((k for k in per if "attn_bf16_kernel" in k), None)
+    attn = next((k for k in per if "attn_bf16_kernel" in k or "attn_f32_kernel" in k), None)
     sg = next((k for k in per if "sg_blend" in k), None)
-    if copy is None or attn is None:
-        raise SystemExit("need the calibration copy and the attention kernel in the counter runs")
+    if attn is None:
+        raise SystemExit("need the attention kernel in the counter runs")
     mean = lambda k, c: statistics.fmean(per[k][c]) if per[k].get(c) else None
-    f_fetch = COPY_BYTES / (mean(copy, "FETCH_SIZE") * 1024) if mean(copy, "FETCH_SIZE") else None
-    f_write = COPY_BYTES / (mean(copy, "WRITE_SIZE") * 1024) if mean(copy, "WRITE_SIZE") else None
+    f_fetch = f_write = None
+    if copy is not None:
+        f_fetch = COPY_BYTES / (mean(copy, "FETCH_SIZE") * 1024) if mean(copy, "FETCH_SIZE") else None
+        f_write = COPY_BYTES / (mean(copy, "WRITE_SIZE") * 1024) if mean(copy, "WRITE_SIZE") else None
+    fmt = lambda f: "n/a" if f is None else f"x{f:.3f}"
     lines = [f"rocprofv3 counter summary -- workload {workload}",
              f"commands (from the repository root), one run per pass: {cmd}",
              f"kernel source hash: {kernel_source_hash()}",
-             f"calibration copy ({COPY_BYTES >> 20} MiB read + written): FETCH_SIZE x{f_fetch:.3f}, WRITE_SIZE x{f_write:.3f}",
+             (f"calibration copy ({COPY_BYTES >> 20} MiB read + written): FETCH_SIZE {fmt(f_fetch)}, "
+              f"WRITE_SIZE {fmt(f_write)}") if copy is not None else "no calibration copy in these runs",
              ""]
     summary = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
                "fetch_scale": f_fetch, "write_scale": f_write}
@@ -107,7 +111,7 @@ def counters(pmc_dirs, workload: str, cmd: str) -> str:
             lines.append(f"    {c:30s} {mean(k, c):16.6g}")
         fetch = mean(k, "FETCH_SIZE")
         write = mean(k, "WRITE_SIZE")
-        if fetch is not None and write is not None:
+        if fetch is not None and write is not None and f_fetch and f_write:
             hbm = fetch * 1024 * f_fetch + write * 1024 * f_write
             lines.append(f"    -> HBM bytes per dispatch (scaled): read {fetch * 1024 * f_fetch / 1e6:.1f} MB, "
                          f"write {write * 1024 * f_write / 1e6:.1f} MB, total {hbm / 1e6:.1f} MB")
