@@ -6,9 +6,10 @@
 // argument"; or a clipped window, "ScaleDiff ...", "Approach").
 //
 // Workgroup = 4 waves, one 16-query tile per wave (64 queries), sharing each
-// K/V block (64 keys; 32 at d = 128) staged in LDS; the next block's global
-// loads are in flight in registers while the current one is computed.  Per
-// block and wave:
+// 32-key K/V block staged in LDS; the next block's global loads are in flight
+// in registers while the current one is computed.  Three workgroups per CU at
+// d <= 64 (two at d = 128, where a third would spill registers).  Per block
+// and wave:
 //
 //   S^T = K Q^T   one 16-key x 16-query tile per 16 keys.  The instruction
 //                 takes A[m][k] from lane (m + 16k), B[k][n] from lane
@@ -44,10 +45,19 @@ constexpr int kQueries = 16 * kWaves;  // queries per workgroup (one 16-query ti
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// j / d for 0 <= j < 2^24 via a float reciprocal and one correction step.
+__device__ __forceinline__ int fast_div(int j, int d, float inv) {
+  int q = (int)((float)j * inv);
+  const int r = j - q * d;
+  q += (r < 0) ? -1 : ((r >= d) ? 1 : 0);
+  return q;
+}
+
+// Token index of entry j of run r (windows: rows of row_len tokens, pitch apart).
 template <int MODE>
-__device__ __forceinline__ int token_of(const Run& r, int j) {
+__device__ __forceinline__ int token_of(const Run& r, int j, float inv_row_len) {
   if (MODE == NPA_MODE_STRIPS) return r.start + j;
-  const int row = j / r.row_len;
+  const int row = fast_div(j, r.row_len, inv_row_len);
   return r.start + row * r.pitch + (j - row * r.row_len);
 }
 
@@ -57,23 +67,23 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
 
 // Token index and source buffer of key j (0 <= j < nk) of the tile's key runs.
 template <int MODE>
-__device__ __forceinline__ int key_token(const TileRuns& tr, int j, bool& stale) {
+__device__ __forceinline__ int key_token(const TileRuns& tr, const float (&inv)[3], int j, bool& stale) {
   if (j < tr.nk[0]) {
     stale = tr.src[0] != 0;
-    return token_of<MODE>(tr.k[0], j);
+    return token_of<MODE>(tr.k[0], j, inv[0]);
   }
   j -= tr.nk[0];
   if (j < tr.nk[1]) {
     stale = tr.src[1] != 0;
-    return token_of<MODE>(tr.k[1], j);
+    return token_of<MODE>(tr.k[1], j, inv[1]);
   }
   stale = tr.src[2] != 0;
-  return token_of<MODE>(tr.k[2], j - tr.nk[1]);
+  return token_of<MODE>(tr.k[2], j - tr.nk[1], inv[2]);
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
-  constexpr int kBN = D == 128 ? 32 : 64;  // keys per LDS block
+__global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(const AttnArgs a) {
+  constexpr int kBN = 32;                  // keys per LDS block
   constexpr int NTL = kBN / 16;            // 16-key tiles per block
   constexpr int LD = D + 4;                // LDS row pitch (floats)
   constexpr int C4 = D / 4;                // 16-byte chunks per key row
@@ -91,12 +101,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
   const int nq = tr.q.count();
   const int nk = tr.nk[0] + tr.nk[1] + tr.nk[2];
   const int64_t bh = (int64_t)bc.b * a.sb + (int64_t)bc.head * a.sh;
+  float inv_len[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) inv_len[r] = tr.k[r].row_len > 0 ? 1.0f / (float)tr.k[r].row_len : 0.0f;
 
   // this lane's query (column l16 of the wave's tile) and its quarter of Q,
   // pre-scaled by scale * log2(e)
   const int qi = bc.qb * kQueries + wave * 16 + l16;
   const bool ok = qi < nq;
-  const int64_t qoff = bh + (int64_t)(ok ? token_of<MODE>(tr.q, qi) : 0) * a.sn;
+  const int64_t qoff = bh + (int64_t)(ok ? token_of<MODE>(tr.q, qi, 1.0f / (float)tr.q.row_len) : 0) * a.sn;
   float qf[DQ];
 #pragma unroll
   for (int e = 0; e < DQ; e += 4) {
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(const AttnArgs a) {
       rv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (j < nk) {
         bool stale;
-        const int64_t off = bh + (int64_t)key_token<MODE>(tr, j, stale) * a.sn + dc * 4;
+        const int64_t off = bh + (int64_t)key_token<MODE>(tr, inv_len, j, stale) * a.sn + dc * 4;
         rk[c] = *(const f32x4*)((const float*)(stale ? a.ks : a.kf) + off);
         rv[c] = *(const f32x4*)((const float*)(stale ? a.vs : a.vf) + off);
       }
