@@ -14,11 +14,11 @@
 //   S^T = K Q^T   one 16-key x 16-query tile per 16 keys.  The instruction
 //                 takes A[m][k] from lane (m + 16k), B[k][n] from lane
 //                 (n + 16k) and leaves D[4g + i][n] in entry i of lane
-//                 (n + 16g).  Lane group
-//                 g supplies the contiguous quarter d in [g*D/4, (g+1)*D/4) of
-//                 the dot product, so its K reads are 16-byte row reads and its
-//                 Q quarter stays in registers.  Lane (n + 16g) ends with the
-//                 scores of keys 4g..4g+3 of each tile for query n.
+//                 (n + 16g).  Lane group g supplies the contiguous quarter
+//                 d in [g*D/4, (g+1)*D/4) of the dot product, so its K reads
+//                 are 16-byte row reads and its Q quarter stays in registers.
+//                 Lane (n + 16g) ends with the scores of keys 4g..4g+3 of each
+//                 tile for query n.
 //   softmax       exact block max (in-lane, then across the four lane groups),
 //                 running max / sum with one rescale of O per block, exp2 of
 //                 scores pre-scaled by scale*log2(e) (folded into Q).
