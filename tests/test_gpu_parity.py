@@ -229,13 +229,14 @@ def test_zero_query_set_means(H, W, spec):
     [(32, 32, A.Strips(4, halo_rows=3), 64), (48, 16, A.Strips(3, halo_rows=5), 128),
      (40, 36, A.Windows(8, 12, 5, 3), 64), (32, 32, A.Windows(16, 16, 4, 4), 128)],
 )
-def test_nan_poisoned_unread_regions(H, W, spec, d):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_nan_poisoned_unread_regions(H, W, spec, d, dt):
     """Fill everything the definition never reads with NaN; the result must be
     finite and equal to the clean run.  Stale copies of a strip's own rows and
     stale rows beyond the halo are poisoned; for one tile, every fresh key
     outside its set is poisoned and only that tile's outputs are checked."""
-    inp = WL.attention_inputs(1, 2, d, H, W, seed=11, dtype="bf16", stale=True)
-    clean = _run(inp, H, W, spec, "bf16")
+    inp = WL.attention_inputs(1, 2, d, H, W, seed=11, dtype=dt, stale=True)
+    clean = _run(inp, H, W, spec, dt)
     tiles = list(A.iter_tiles(H, W, spec))
     used_stale = np.zeros(H * W, dtype=bool)
     for _, _, st in tiles:
@@ -258,7 +259,7 @@ def test_nan_poisoned_unread_regions(H, W, spec, d):
         other[st] = False
         a[:, other] = np.nan
         pois[n] = a
-    got = _run(pois, H, W, spec, "bf16")
+    got = _run(pois, H, W, spec, dt)
     assert np.isfinite(got[:, qt]).all()
     np.testing.assert_array_equal(got[:, qt], clean[:, qt])
 
