@@ -130,7 +130,7 @@ def test_workload_full_size_sampled(name):
         assert err <= ATOL[w["dtype"]], f"{name} (b={b}, head={j}): max abs err {err}"
 
 
-@pytest.mark.parametrize("name", ["sdxl2048_strips", "flux4096_npa", "sdxl1024_strips"])
+@pytest.mark.parametrize("name", ["sdxl2048_strips", "flux4096_npa", "sdxl1024_strips", "pcpp_tiny_fp32"])
 def test_repeated_calls_are_bitwise_identical(name):
     """The kernels use no atomics and no order-dependent reduction across
     workgroups, so the same call gives the same bits every time; a race on the
