@@ -148,7 +148,7 @@ def main() -> int:
     from partial_context_patch_amd import npa, profiling
     from partial_context_patch_amd import workloads as WL
 
-    npa.load(build_if_missing=False)
+    npa.load()  # builds the library in-tree only when none is built
     name = args.workload
     w = WL.ATTENTION_WORKLOADS[name]
     if args.dtype is not None:
