@@ -233,7 +233,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
     block_m = npa::attn_bf16_block_m(L->head_dim, false);
   } else if (L->dtype == NPA_F32) {
     esize = 4;
-    block_m = npa::attn_f32_block_m(L->head_dim);
+    block_m = npa::attn_f32_block_m(L->head_dim, false);
   } else {
     return fail(NPA_ERR_INVALID_ARG, "unknown dtype %d", L->dtype);
   }
@@ -302,6 +302,18 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
       grid(npa::attn_bf16_block_m(L->head_dim, true));
     }
   }
+  // f32: a grid with fewer workgroups than the GPU has CUs runs in the
+  // key-split shape where there is one (four times the workgroups, each
+  // walking a quarter of the keys)
+  bool split = false;
+  if (L->dtype == NPA_F32) {
+    const int cus = cu_count();
+    const int bm = npa::attn_f32_block_m(L->head_dim, true);
+    if (cus > 0 && bm > 0 && nblocks < cus) {
+      split = true;
+      grid(bm);
+    }
+  }
   if (nblocks >= (int64_t(1) << 31))
     return fail(NPA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)nblocks);
   a.nblocks = (int32_t)nblocks;
@@ -314,7 +326,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const hipError_t e = (L->dtype == NPA_BF16) ? npa::launch_attn_bf16(a, L->head_dim, small, s)
-                                              : npa::launch_attn_f32(a, L->head_dim, block_m, s);
+                                              : npa::launch_attn_f32(a, L->head_dim, split, s);
   if (e != hipSuccess) return fail(NPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

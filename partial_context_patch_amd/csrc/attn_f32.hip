@@ -30,6 +30,14 @@
 //                 row, and at the end a lane holds 4*DT consecutive channels
 //                 of its query's output row.
 //
+// Key-split shape, for calls whose grid would leave most CUs idle (d <= 64):
+// the four waves share one 16-query tile and wave w takes the 32-key blocks
+// w, w + 4, w + 8, ... of its keys, staged by itself in its own LDS region
+// (wave-level synchronisation only); at the end the waves' running max, sum
+// and output are merged through LDS (out = sum_w 2^(m_w - M) O_w / sum_w
+// 2^(m_w - M) l_w with M = max_w m_w).  Four times the workgroups, each a
+// quarter as long.
+//
 // This is the accuracy path for fp32 inputs; products and sums stay in fp32.
 #include <hip/hip_runtime.h>
 
@@ -41,6 +49,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;  // threads per workgroup
 constexpr int kQueries = 16 * kWaves;  // queries per workgroup (one 16-query tile per wave)
+constexpr int kSplitQueries = 16;      // key-split shape: one tile for the whole workgroup
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -81,20 +90,33 @@ __device__ __forceinline__ int key_token(const TileRuns& tr, const float (&inv)[
   return token_of<MODE>(tr.k[2], j - tr.nk[1], inv[2]);
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(const AttnArgs a) {
-  constexpr int kBN = 32;                  // keys per LDS block
-  constexpr int NTL = kBN / 16;            // 16-key tiles per block
-  constexpr int LD = D + 4;                // LDS row pitch (floats)
-  constexpr int C4 = D / 4;                // 16-byte chunks per key row
-  constexpr int CH = kBN * C4 / kThreads;  // chunks per thread per K (and V) block
-  constexpr int DQ = D / 4;                // channels per lane group in S^T
-  constexpr int DT = D / 16;               // 16-dim steps of O^T
-  static_assert(CH * kThreads == kBN * C4 && DT >= 2 && DT % 2 == 0, "shape");
-  __shared__ __attribute__((aligned(16))) float sk[kBN * LD];
-  __shared__ __attribute__((aligned(16))) float sv[kBN * LD];
+// Wave-level barrier: the wave's LDS writes before it are visible to its reads after it.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int MODE, bool SPLIT>
+__global__ __launch_bounds__(kThreads, (SPLIT ? 1 : (D == 128 ? 2 : 3))) void attn_f32_kernel(const AttnArgs a) {
+  constexpr int kBN = 32;                   // keys per LDS block
+  constexpr int NTL = kBN / 16;             // 16-key tiles per block
+  constexpr int LD = D + 4;                 // LDS row pitch (floats)
+  constexpr int C4 = D / 4;                 // 16-byte chunks per key row
+  constexpr int NTHR = SPLIT ? 64 : kThreads;  // threads staging one block
+  constexpr int CH = kBN * C4 / NTHR;       // chunks per thread per K (and V) block
+  constexpr int DQ = D / 4;                 // channels per lane group in S^T
+  constexpr int DT = D / 16;                // 16-dim steps of O^T
+  constexpr int NBUF = SPLIT ? kWaves : 1;  // LDS block buffers (one per wave when split)
+  static_assert(CH * NTHR == kBN * C4 && DT >= 2 && DT % 2 == 0, "shape");
+  static_assert(!SPLIT || kWaves * 16 * (D + 2) <= NBUF * kBN * LD, "merge buffer");
+  __shared__ __attribute__((aligned(16))) float sk[NBUF * kBN * LD];
+  __shared__ __attribute__((aligned(16))) float sv[NBUF * kBN * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int stid = SPLIT ? lane : tid;  // index among the threads staging a block
+  float* const skw = sk + (SPLIT ? wave * kBN * LD : 0);
+  float* const svw = sv + (SPLIT ? wave * kBN * LD : 0);
   const int g4 = lane >> 4, l16 = lane & 15;
   const BlockCoord bc = decode_block(a, blockIdx.x, false);
   const TileRuns tr = tile_runs(a.g, bc.tile);
@@ -107,7 +129,7 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
 
   // this lane's query (column l16 of the wave's tile) and its quarter of Q,
   // pre-scaled by scale * log2(e)
-  const int qi = bc.qb * kQueries + wave * 16 + l16;
+  const int qi = SPLIT ? bc.qb * kSplitQueries + l16 : bc.qb * kQueries + wave * 16 + l16;
   const bool ok = qi < nq;
   const int64_t qoff = bh + (int64_t)(ok ? token_of<MODE>(tr.q, qi, 1.0f / (float)tr.q.row_len) : 0) * a.sn;
   float qf[DQ];
@@ -124,12 +146,12 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
   float m = -INFINITY;  // running max of the query's scores (log2 domain)
   float l = 0.0f;       // sum of this lane's weights (its keys 4g4..4g4+3 of every tile)
 
-  // K/V block staging: chunk c of this thread is key (tid + c*kThreads) / C4
+  // K/V block staging: chunk c of this thread is key (stid + c*NTHR) / C4
   f32x4 rk[CH], rv[CH];
   auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * kThreads, key = idx / C4, dc = idx % C4;
+      const int idx = stid + c * NTHR, key = idx / C4, dc = idx % C4;
       const int j = k0 + key;
       rk[c] = f32x4{0.f, 0.f, 0.f, 0.f};
       rv[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -144,18 +166,26 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int idx = tid + c * kThreads, key = idx / C4, dc = idx % C4;
-      *(f32x4*)&sk[key * LD + dc * 4] = rk[c];
-      *(f32x4*)&sv[key * LD + dc * 4] = rv[c];
+      const int idx = stid + c * NTHR, key = idx / C4, dc = idx % C4;
+      *(f32x4*)&skw[key * LD + dc * 4] = rk[c];
+      *(f32x4*)&svw[key * LD + dc * 4] = rv[c];
     }
   };
+  // the threads that stage a block agree it is complete (or consumed)
+  auto sync = [&]() __attribute__((always_inline)) {
+    if (SPLIT)
+      wave_sync();
+    else
+      __syncthreads();
+  };
 
-  load(0);
-  for (int k0 = 0; k0 < nk; k0 += kBN) {
-    __syncthreads();  // every wave is done with the previous block
+  const int kfirst = SPLIT ? wave * kBN : 0, kstep = SPLIT ? kWaves * kBN : kBN;
+  if (kfirst < nk) load(kfirst);
+  for (int k0 = kfirst; k0 < nk; k0 += kstep) {
+    sync();  // done with the previous block
     store();
-    __syncthreads();
-    if (k0 + kBN < nk) load(k0 + kBN);
+    sync();
+    if (k0 + kstep < nk) load(k0 + kstep);
     const int nvalid = nk - k0 < kBN ? nk - k0 : kBN;
 
     // S^T, the block's 16-key tiles interleaved (independent accumulation chains)
@@ -166,7 +196,7 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
     for (int e = 0; e < DQ; e += 4) {
       f32x4 kv[NTL];
 #pragma unroll
-      for (int t = 0; t < NTL; ++t) kv[t] = *(const f32x4*)&sk[(16 * t + l16) * LD + g4 * DQ + e];
+      for (int t = 0; t < NTL; ++t) kv[t] = *(const f32x4*)&skw[(16 * t + l16) * LD + g4 * DQ + e];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -207,7 +237,7 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
     for (int t = 0; t < NTL; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float* vr = &sv[(16 * t + 4 * g4 + j) * LD + l16 * DT];
+        const float* vr = &svw[(16 * t + 4 * g4 + j) * LD + l16 * DT];
         float vv[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; dt += 2) {
@@ -223,6 +253,42 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
   // the query's keys are spread over the four lane groups
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
+  if (SPLIT) {
+    // merge the four waves' partial results for the shared 16 queries, through
+    // LDS: per wave 16 maxima, 16 sums and 16 output rows (channel order as in o)
+    __syncthreads();  // every wave is done with its blocks
+    float* rm = sk;                    // [kWaves][16]
+    float* rl = sk + kWaves * 16;      // [kWaves][16]
+    float* ro = sk + 2 * kWaves * 16;  // [kWaves][16][D]
+    if (g4 == 0) {
+      rm[wave * 16 + l16] = m;
+      rl[wave * 16 + l16] = lt;
+    }
+    float* my = ro + (wave * 16 + l16) * D + 4 * g4 * DT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) my[i * DT + dt] = o[dt][i];
+    __syncthreads();
+    if (wave != 0) return;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, rm[w * 16 + l16]);
+    const float msh = (mx == -INFINITY) ? 0.0f : mx;
+    lt = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = __builtin_amdgcn_exp2f(rm[w * 16 + l16] - msh);
+      lt += f * rl[w * 16 + l16];
+      const float* src = ro + (w * 16 + l16) * D + 4 * g4 * DT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][i] += f * src[i * DT + dt];
+    }
+  }
   if (!ok) return;
   const float inv = 1.0f / lt;
   // entry i of o[dt] is channel (4*g4 + i)*DT + dt
@@ -236,26 +302,28 @@ __global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 3)) void attn_f32_kernel(
     }
 }
 
-template <int D>
+template <int D, bool SPLIT>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.nblocks), block(kThreads);
   if (a.g.mode == NPA_MODE_STRIPS)
-    hipLaunchKernelGGL((attn_f32_kernel<D, NPA_MODE_STRIPS>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, NPA_MODE_STRIPS, SPLIT>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<D, NPA_MODE_WINDOW>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, NPA_MODE_WINDOW, SPLIT>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_f32_block_m(int head_dim) {
+int attn_f32_block_m(int head_dim, bool split) {
+  if (split) return (head_dim == 32 || head_dim == 64) ? kSplitQueries : 0;
   return (head_dim == 32 || head_dim == 64 || head_dim == 128) ? kQueries : 0;
 }
 
-hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int /*block_m*/, hipStream_t st) {
-  if (head_dim == 32) return launch_d<32>(a, st);
-  if (head_dim == 64) return launch_d<64>(a, st);
-  return launch_d<128>(a, st);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool split, hipStream_t st) {
+  if (split) return head_dim == 32 ? launch_d<32, true>(a, st) : launch_d<64, true>(a, st);
+  if (head_dim == 32) return launch_d<32, false>(a, st);
+  if (head_dim == 64) return launch_d<64, false>(a, st);
+  return launch_d<128, false>(a, st);
 }
 
 }  // namespace npa

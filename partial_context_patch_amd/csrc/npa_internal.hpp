@@ -190,12 +190,13 @@ struct SgArgs {
 };
 
 // Launchers (return the HIP error of the launch).
-// bf16: `small` selects the small-launch workgroup shape (see attn_bf16.hip).
+// bf16: `small` selects the small-launch workgroup shape (see attn_bf16.hip);
+// f32: `split` selects the key-split shape (see attn_f32.hip).
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool small, hipStream_t st);
-hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int block_m, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, bool split, hipStream_t st);
 int attn_bf16_block_m(int head_dim, bool small);  // queries per workgroup, 0 if unsupported
 int attn_bf16_per_cu(int head_dim, bool small);   // workgroups resident per CU
-int attn_f32_block_m(int head_dim);
+int attn_f32_block_m(int head_dim, bool split);   // queries per workgroup, 0 if unsupported
 hipError_t launch_sg_blend(const SgArgs& a, hipStream_t st);
 hipError_t launch_asg_blend(const float* eps, const float* ref, const float* mask, float* out,
                             int64_t count, float w, hipStream_t st);

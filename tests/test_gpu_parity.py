@@ -512,6 +512,31 @@ def test_strided_views_match_contiguous_bit_for_bit(dt):
     assert np.array_equal(got, want)
 
 
+# fp32: calls whose regular grid has fewer workgroups than the GPU has CUs
+# run the key-split shape (every small f32 case above does, at d <= 64); these
+# are sized so that the regular 64-query shape runs.
+F32_REGULAR = [
+    # (H, W, B, Hh, d, spec)
+    (32, 32, 1, 80, 64, A.Strips(4, halo_rows=3)),
+    (24, 20, 2, 60, 32, A.Windows(8, 10, 3, 2)),
+    (16, 16, 1, 64, 64, A.Windows(8, 8, 2, 2, 7)),
+]
+
+
+@pytest.mark.parametrize("H,W,B,Hh,d,spec", F32_REGULAR)
+def test_f32_regular_shape_full_compare(H, W, B, Hh, d, spec):
+    T = A.text_tokens(spec)
+    tiles = list(A.iter_tiles(H, W, spec))
+    n_map = len(tiles) - (1 if T else 0)
+    nq = len(tiles[0][0])
+    grid = B * Hh * (n_map * -(-nq // 64) + (-(-T // 64) if T else 0))
+    assert grid >= torch.cuda.get_device_properties(0).multi_processor_count, "case too small for the regular shape"
+    inp = WL.attention_inputs(B, Hh, d, H, W, seed=78, dtype="f32", text_tokens=T)
+    got = _run(inp, H, W, spec, "f32")
+    ref = A.attention_tier1(inp["q"], inp["k"], inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec)
+    assert np.abs(got - ref).max() <= ATOL["f32"]
+
+
 def test_calls_replay_from_a_hip_graph():
     """npa_attn_fwd and npa_sg_blend captured into one HIP graph: every replay
     (with eager work and synchronisations between replays) reproduces the
