@@ -131,7 +131,10 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
                           const npa_layout_t* layout, const npa_halo_t* halo,
                           void* out, void* hip_stream);
 
-/* Host-only planner (no GPU needed).  Writes up to `capacity` tile
+/* Host-only planner (no GPU needed): the key sets defined at the top of this
+ * file (PCPP review page, "What carries the argument"; ScaleDiff page,
+ * "Approach"), written out per query tile as runs of tokens -- the same
+ * closed form every workgroup of npa_attn_fwd evaluates.  Writes up to `capacity` tile
  * descriptors into `tiles` (may be NULL with capacity 0), the total tile
  * count into *n_tiles and the number of attended (query, key) pairs per
  * (batch, head) into *useful_pairs_per_bh (either output may be NULL). */
@@ -140,11 +143,18 @@ npa_status_t npa_plan(const npa_layout_t* layout, const npa_halo_t* halo,
                       int64_t* useful_pairs_per_bh);
 
 /* Useful attention flops of one npa_attn_fwd call:
- * 4 * head_dim * attended pairs * batch * heads; -1 on invalid arguments. */
+ * 4 * head_dim * attended pairs * batch * heads; -1 on invalid arguments.
+ * Only (query, key) pairs inside the key sets defined above count -- 2*d
+ * flops for the score and 2*d for the weighted value sum of each pair --
+ * so padding, masked keys and the softmax itself add nothing.  This is the
+ * work measure behind the useful partial-attention throughput (the pages
+ * report only end-to-end times; the partial key set is the compute saving
+ * the PCPP review page's "Core claim" and the ScaleDiff page's "Approach"
+ * attribute to the method). */
 int64_t npa_useful_flops(const npa_layout_t* layout, const npa_halo_t* halo);
 
 /* Structure-guidance blend: "ScaleDiff ..." (atlas.scime.ai), "Approach"
- * (low-frequency structure guidance in latent space):
+ * (the latent's low frequencies are pulled towards those of a reference):
  *   out = x + w_t * (G_sigma * ref - G_sigma * x)     per channel,
  * G_sigma a separable Gaussian with taps |k| <= ceil(3*sigma), weights
  * exp(-k^2/(2 sigma^2)) normalised to 1, reflect-101 borders.

@@ -17,9 +17,11 @@ Sources (web pages, cited by title and section):
   the attention is multi-head scaled dot-product attention.
 * "ScaleDiff: Higher-Resolution Image Synthesis via Efficient and
   Model-Agnostic Diffusion" (atlas.scime.ai summary) -- section "Approach":
-  non-overlapping query patches, each attending to an overlapping key/value
-  neighbourhood (Neighborhood Patch Attention); low-frequency structure
-  guidance in latent space.
+  the query tiles partition the token map, and the keys/values of a tile are
+  its own rectangle grown by a halo on every side and clipped at the map
+  border, so neighbouring tiles share keys (Neighborhood Patch Attention);
+  the same section adds a guidance step that pulls the latent's low
+  frequencies towards a reference.
 
 Modules:
   attention -- membership predicates, tier-0 (per-pair loops) and tier-1

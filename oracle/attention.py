@@ -153,8 +153,12 @@ def attended_sets(H: int, W: int, spec) -> list:
     return out
 
 
-def attention_tier0(q, k, v, k_stale, v_stale, H: int, W: int, spec, scale: Optional[float] = None):
-    """Brute force: Python loops over every (query, key, channel)."""
+def attention_tier0(q, k, v, k_stale, v_stale, H: int, W: int, spec, scale: Optional[float] = None,
+                    query_tokens: Optional[Sequence[int]] = None, heads: Optional[Iterable[Tuple[int, int]]] = None):
+    """Brute force: Python loops over every (query, key, channel).
+
+    query_tokens / heads -- if given, only those queries / (batch, head) pairs
+    are computed; the other outputs stay NaN (a bounded sample for timing)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -164,28 +168,30 @@ def attention_tier0(q, k, v, k_stale, v_stale, H: int, W: int, spec, scale: Opti
     if k_stale is not None:
         k_stale = np.asarray(k_stale, dtype=np.float64)
         v_stale = np.asarray(v_stale, dtype=np.float64)
-    out = np.zeros((B, N, Hh, v.shape[-1]))
+    sample = query_tokens is not None or heads is not None
+    out = np.full((B, N, Hh, v.shape[-1]), np.nan) if sample else np.zeros((B, N, Hh, v.shape[-1]))
     sets = attended_sets(H, W, spec)
-    for b in range(B):
-        for j in range(Hh):
-            for t in range(N):
-                fresh, stale = sets[t]
-                keys = [(k[b, kk, j], v[b, kk, j]) for kk in fresh]
-                keys += [(k_stale[b, kk, j], v_stale[b, kk, j]) for kk in stale]
-                logits = []
-                for kvec, _ in keys:
-                    acc = 0.0
-                    for e in range(d):
-                        acc += q[b, t, j, e] * kvec[e]
-                    logits.append(scale * acc)
-                m = max(logits)
-                w = [math.exp(x - m) for x in logits]
-                z = sum(w)
-                for e in range(v.shape[-1]):
-                    acc = 0.0
-                    for wk, (_, vvec) in zip(w, keys):
-                        acc += wk * vvec[e]
-                    out[b, t, j, e] = acc / z
+    bh = list(heads) if heads is not None else [(b, j) for b in range(B) for j in range(Hh)]
+    qs = list(query_tokens) if query_tokens is not None else range(N)
+    for b, j in bh:
+        for t in qs:
+            fresh, stale = sets[t]
+            keys = [(k[b, kk, j], v[b, kk, j]) for kk in fresh]
+            keys += [(k_stale[b, kk, j], v_stale[b, kk, j]) for kk in stale]
+            logits = []
+            for kvec, _ in keys:
+                acc = 0.0
+                for e in range(d):
+                    acc += q[b, t, j, e] * kvec[e]
+                logits.append(scale * acc)
+            m = max(logits)
+            w = [math.exp(x - m) for x in logits]
+            z = sum(w)
+            for e in range(v.shape[-1]):
+                acc = 0.0
+                for wk, (_, vvec) in zip(w, keys):
+                    acc += wk * vvec[e]
+                out[b, t, j, e] = acc / z
     return out
 
 

@@ -183,11 +183,13 @@ __global__ __launch_bounds__(NTH) void sg_blend_tile(const SgArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* __restrict__ eps,
-                                                             const float* __restrict__ ref,
-                                                             const float* __restrict__ mask,
-                                                             float* out, int64_t n4, int64_t count,
-                                                             float w) {
+// out may be one of the inputs itself (an in-place update): no pointer is
+// marked __restrict__, since out is written while the same memory is read
+// through the input pointers.  Each element is read before its own store and
+// never again, so the in-place form is well defined.
+__global__ __launch_bounds__(kThreads) void asg_blend_kernel(const float* eps, const float* ref,
+                                                             const float* mask, float* out, int64_t n4,
+                                                             int64_t count, float w) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {

@@ -27,7 +27,7 @@ from typing import Dict, Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("csrc/attn_bf16.hip", "csrc/npa_internal.hpp")
+KERNEL_SOURCES = ("csrc/attn_bf16.hip", "csrc/npa_internal.hpp", "csrc/api.cpp")
 COPY_BYTES = 512 << 20
 
 

@@ -88,13 +88,22 @@ STALE_NOISE_STD = 0.05
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
-    """Round fp32 values to the nearest bf16 (ties to even); returned as fp32."""
+    """Round fp32 values to the nearest bf16 (ties to even); returned as fp32.
+
+    On the bit pattern u: add 0x7FFF plus the lowest kept bit, clear the low
+    16 bits.  For every finite or infinite value u + 0x8000 stays below 2^32,
+    so 32-bit arithmetic is exact; NaNs are passed through unchanged."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
-    return np.where(np.isnan(a), a, out)
+    u = a.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = a[nan]
+    return out
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -34,3 +34,14 @@ def test_cpu_baseline_times_the_oracle_on_a_sample():
     assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s"
     assert res["value"] > 0 and res["cores"] >= 1
     assert "units of 8" in res["sample"]  # 2 heads x 4 strips
+
+
+def test_tier0_baseline_times_the_brute_force_oracle():
+    """The tier-0 entry of cpu_baseline runs the oracle's Python loops on a
+    bounded sample of the tiny strip layer and reports a useful-flop rate."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    res = bench.cpu_tier0(budget_s=0.3)
+    assert res["kind"] == "oracle" and res["unit"] == "TFLOP/s" and res["value"] > 0
+    assert "tier 0" in res["sample"] and "pcpp_tiny_fp32" in res["sample"]
