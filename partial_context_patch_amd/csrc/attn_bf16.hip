@@ -39,8 +39,14 @@
 //     the common path has no max, no rescale of O and no branch per query; if
 //     a row sum ends outside [1, 2^60] (checked from the sums themselves) the
 //     workgroup computes the true row maxima and runs the tile again with them;
-//   * row sums come from v_dot2c_f32_bf16 on the packed bf16 P, i.e. the
-//     denominator sums exactly the weights the numerator uses.
+//   * row sums run on the matrix core too: one more 16x16x32 MFMA per 32-key
+//     step and 16-query tile, with an all-ones A operand and the packed bf16
+//     P as B, leaves the query's sum in every accumulator entry -- the
+//     denominator sums exactly the weights the numerator uses, with the same
+//     fp32 accumulation.  At d = 64 that is one MFMA more per eight; the VALU
+//     alternatives cost more (v_dot2c_f32_bf16 does not co-issue with MFMAs:
+//     measured ~12 cycles per dot2c beside a dense MFMA stream, and the fp32
+//     adds of the weights do not fit beside the exps).
 // Loads and stores go through buffer descriptors: out-of-range keys and
 // queries read zeros / drop their stores without branches.
 #include <hip/hip_runtime.h>
@@ -54,7 +60,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -110,18 +115,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+// max over the four 16-lane groups (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float quad_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
   x = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-  x = __int_as_float(r[0]) + __int_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 __device__ __forceinline__ float max4(const f32x4& a) { return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])); }
 
@@ -163,9 +162,8 @@ __device__ __forceinline__ int run_token(const Run& r, int j, float inv_len) {
 }
 
 // exp2 of the 8 accumulator entries of one lane for a 32-key step (tiles 0
-// and 1), packed to bf16 in key order as the PV B operand; returns s plus the
-// sum of the packed (bf16) weights.
-__device__ __forceinline__ float exp_pack(const f32x4& a0, const f32x4& a1, float shift, bf16x8& p, float s) {
+// and 1), packed to bf16 in key order as the PV B operand.
+__device__ __forceinline__ void exp_pack(const f32x4& a0, const f32x4& a1, float shift, bf16x8& p) {
   f32x8 e;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -173,14 +171,10 @@ __device__ __forceinline__ float exp_pack(const f32x4& a0, const f32x4& a1, floa
     e[4 + i] = __builtin_amdgcn_exp2f(a1[i] - shift);
   }
   p = __builtin_convertvector(e, bf16x8);
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, s, false);
-  return s;
 }
 
 // Same without a shift argument (the common path: the shift is inside acc).
-__device__ __forceinline__ float exp_pack0(const f32x4& a0, const f32x4& a1, bf16x8& p, float s) {
+__device__ __forceinline__ void exp_pack0(const f32x4& a0, const f32x4& a1, bf16x8& p) {
   f32x8 e;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -188,10 +182,6 @@ __device__ __forceinline__ float exp_pack0(const f32x4& a0, const f32x4& a1, bf1
     e[4 + i] = __builtin_amdgcn_exp2f(a1[i]);
   }
   p = __builtin_convertvector(e, bf16x8);
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, s, false);
-  return s;
 }
 
 
@@ -380,7 +370,9 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
 
   f32x4 o[DT][NT];
   f32x4 shift[NT];  // -m in every entry: C operand of the first S^T MFMA
-  float l[NT];
+  f32x4 l[NT];      // row sums, from the ones MFMA: every entry holds the query's sum
+  const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
   // K row this lane feeds into the S^T tile h (0, 1) of a 32-key step: rows
   // are permuted so that the tiles' accumulator entries of lane group g4 are
@@ -488,7 +480,8 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
             for (int nt = 0; nt < NT; ++nt) sc[h][nt][i] = -INFINITY;
     };
     // O^T += V^T P^T over step s: per 16-dim tile one V^T fragment (keys
-    // 8*g4 .. +8 of the step, from two transposed reads of four key rows)
+    // 8*g4 .. +8 of the step, from two transposed reads of four key rows);
+    // then the row sums: ones * P^T adds the step's weights of each query
     auto pv = [&](int s, const bf16x8 (&p)[NT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -502,6 +495,8 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma16(vf, p[nt], o[dt][nt]);
       }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) l[nt] = mfma16(ones, p[nt], l[nt]);
     };
 
     f32x4 s0[2][NT], s1[2][NT];
@@ -515,7 +510,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
       for (int nt = 0; nt < NT; ++nt) {
         float m = fmaxf(max4(s0[0][nt]), max4(s0[1][nt]));
         m = quad_max(m);
-        l[nt] = exp_pack(s0[0][nt], s0[1][nt], m, pa[nt], l[nt]);
+        exp_pack(s0[0][nt], s0[1][nt], m, pa[nt]);
         shift[nt] = f32x4{-m, -m, -m, -m};
       }
       pv(0, pa);
@@ -523,7 +518,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
       scores_raw(skb, 1, s1, false);
       if (part) mask(1, s1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[0][nt], s1[1][nt], pb[nt], l[nt]);
+      for (int nt = 0; nt < NT; ++nt) exp_pack0(s1[0][nt], s1[1][nt], pb[nt]);
       pv(1, pb);
       return;
     }
@@ -532,14 +527,14 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     // weights (one region: the compiler interleaves them)
     scores_raw(skb, 1, s1, false);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s0[0][nt], s0[1][nt], pa[nt], l[nt]);
+    for (int nt = 0; nt < NT; ++nt) exp_pack0(s0[0][nt], s0[1][nt], pa[nt]);
     __builtin_amdgcn_sched_barrier(0);
     if (part) mask(1, s1);
     __builtin_amdgcn_sched_barrier(0);
     // step 0's PV MFMAs run while the VALU does step 1's weights (one region)
     pv(0, pa);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l[nt] = exp_pack0(s1[0][nt], s1[1][nt], pb[nt], l[nt]);
+    for (int nt = 0; nt < NT; ++nt) exp_pack0(s1[0][nt], s1[1][nt], pb[nt]);
     __builtin_amdgcn_sched_barrier(0);
     pv(1, pb);
   };
@@ -548,7 +543,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt][nt] = f32x4{};
-      l[nt] = 0.0f;
+      l[nt] = f32x4{};
     }
     cursor_reset();
     fetch(sk0, sv0);
@@ -578,7 +573,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
     if (preset) break;
     bool bad = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bad |= !(quad_sum(l[nt]) <= kOverflow);
+    for (int nt = 0; nt < NT; ++nt) bad |= !(l[nt][0] <= kOverflow);
     __syncthreads();
     if (wave_any(bad) && lane == 0) redo = 1;  // every writer stores 1
     __syncthreads();
@@ -593,7 +588,7 @@ __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB))
   // ---- normalise and store: lane (query l16, group g4) holds dims 16dt + 4g4 .. +4
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float inv = 1.0f / quad_sum(l[nt]);
+    const float inv = 1.0f / l[nt][0];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f32x4 v;
