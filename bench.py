@@ -240,24 +240,33 @@ def main() -> int:
         # settle: the shader clock ramps up over a second or two of sustained
         # load; a diffusion sampler keeps the GPU busy for far longer than that,
         # so steps are timed at the sustained clock
+        # (batches of 10 steps; the host waits on the batch before the last one,
+        # so the GPU's queue never runs dry and the clock sees no idle gaps)
         t_settle = time.perf_counter()
         n_settle = 0
+        pending = []
         while time.perf_counter() - t_settle < args.settle:
             for _ in range(10):
                 step()
             n_settle += 10
-            torch.cuda.synchronize()
+            e = torch.cuda.Event()
+            e.record()
+            pending.append(e)
+            if len(pending) > 2:
+                pending.pop(0).synchronize()
         if args.settle > 0:
             log(f"settled the clock with {n_settle} steps in {time.perf_counter() - t_settle:.1f} s")
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # the GPU's shader clock and board power, sampled from sysfs while the
+        # timed steps run; started before the synchronisation below, so that
+        # nothing but the launch latency separates the last warm-up step from the
+        # first timed one (after an idle gap of a few ms the clock governor takes
+        # several launches to come back to its sustained level)
+        sampler = profiling.ClockSampler().start()
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        # the GPU's shader clock and board power, sampled from sysfs while the
-        # timed steps run
-        sampler = profiling.ClockSampler().start()
         wall0 = time.perf_counter()
         start.record()
         for i in range(args.steps):

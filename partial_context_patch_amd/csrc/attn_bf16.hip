@@ -131,15 +131,21 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 //   K fragments, ds_read_b128: each 8 lanes read one chunk of rows
 //     {0..3, 8..11} (+ 4h + 16j);
 //   V^T fragments, ds_read_b64_tr_b16: each 32 lanes read two adjacent
-//     chunks of rows {0..3, 8..11} (+ 32s + 16j).
+//     chunks of rows {0..3, 8..11} (+ 32s + 16j), the fragment's second half
+//     the same rows + 4.
+// The masks depend on bits 0, 1 and 3 of the row only: rows r and r + 4 (the
+// second score tile, the second half of a V^T fragment) share their mask, so
+// those reads are the first ones' addresses plus an immediate offset and need
+// no address registers of their own.
 // d = 64 (two rows per 256 bytes): within each row parity the rows 0..3,
 // 8..11 get XOR masks {0, 4, 2, 6}, all differing above bit 0, so both
 // patterns hit distinct slots.  d = 128 (one row per 256 bytes): the eight
-// rows get eight masks that differ above bit 0.
+// rows get the eight even masks {0, 4, 8, 12, 2, 6, 10, 14}, distinct above
+// bit 0 (a pair of adjacent chunks stays a pair).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if (D == 64) return ((r & 3) << 1) ^ (((r >> 3) & 1) << 1);
-  return ((r & 3) << 2) | ((r >> 2) & 3);
+  return ((r & 3) << 2) | (((r >> 3) & 1) << 1);
 }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
