@@ -278,6 +278,67 @@ def test_sg_blend(shape, sigma, w):
     assert err <= 1e-5, f"max abs err {err}"
 
 
+@pytest.mark.parametrize(
+    "shape,sigma,w",
+    [((1, 2, 37, 68), 4.0, 0.5),      # partial tiles on both axes
+     ((1, 1, 100, 128), 1.5, 0.7),    # R = 5: staged radius 8, taps shifted by 3
+     ((1, 3, 130, 132), 5.25, 0.5),   # R = 16, the largest matrix-core radius
+     ((2, 1, 64, 64), 0.3, 1.0),      # R = 1
+     ((1, 1, 17, 20), 4.0, -0.4)],    # a 17 x 20 image inside one tile
+)
+def test_sg_blend_matrix_core_shapes(shape, sigma, w):
+    """Shapes the matrix-core blend takes (W a multiple of 4, R <= 16): tile
+    edges, shifted taps, one-tile images, against the fp64 oracle."""
+    seed = sum(shape) + 11
+    x, ref = WL.sg_inputs(shape[1], shape[2], shape[3], seed=seed, batch=shape[0])
+    out = npa.sg_blend(torch.from_numpy(x).cuda(), torch.from_numpy(ref).cuda(), w, sigma)
+    torch.cuda.synchronize()
+    exp = G.sg_blend(x, ref, w, sigma)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - exp).max()
+    assert err <= 1e-5, f"max abs err {err}"
+
+
+@pytest.mark.parametrize("scale", [2.0**-60, 2.0**-20, 2.0**20, 2.0**60])
+def test_sg_blend_magnitudes(scale):
+    """The matrix-core blend scales each tile by a power of two before its f16
+    split: inputs far from unit size keep fp32-like relative accuracy, and one
+    plane 2^40 smaller than its neighbour plane is not swamped by it."""
+    x, ref = (a[0] for a in WL.sg_inputs(2, 128, 128, seed=5))
+    x = (x * scale).astype(np.float32)
+    ref = (ref * scale).astype(np.float32)
+    x[1] *= np.float32(2.0**-40)
+    ref[1] *= np.float32(2.0**-40)
+    out = npa.sg_blend(torch.from_numpy(x[None]).cuda(), torch.from_numpy(ref[None]).cuda(), 0.5, 4.0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0].astype(np.float64)
+    exp = G.sg_blend(x, ref, 0.5, 4.0)
+    for c in range(2):
+        mag = np.abs(exp[c]).max()
+        err = np.abs(got[c] - exp[c]).max()
+        assert err <= 1e-5 * mag, f"plane {c}: rel err {err / mag}"
+
+
+def test_sg_blend_non_finite_inputs():
+    """A tile holding inf or NaN takes the fp32 path: infinities and NaNs reach
+    exactly the outputs whose windows hold them, as in the fp64 oracle, and
+    every other output stays within the tolerance."""
+    x, ref = (a[0] for a in WL.sg_inputs(3, 192, 256, seed=9))
+    ref[0, 70, 100] = np.inf          # one +inf
+    x[1, 5, 250] = np.nan             # a NaN at the right border
+    ref[2, 150, 3] = np.inf           # inf - inf in the difference
+    x[2, 150, 3] = np.inf
+    out = npa.sg_blend(torch.from_numpy(x[None]).cuda(), torch.from_numpy(ref[None]).cuda(), 0.5, 4.0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0].astype(np.float64)
+    exp = G.sg_blend(x, ref, 0.5, 4.0)
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    assert np.array_equal(np.isposinf(got), np.isposinf(exp))
+    assert np.array_equal(np.isneginf(got), np.isneginf(exp))
+    fin = np.isfinite(exp)
+    assert fin.sum() > 0.9 * fin.size
+    assert np.abs(got[fin] - exp[fin]).max() <= 1e-5
+
+
 def test_sg_blend_workload_is_lfm_at_w1():
     w = WL.SG_WORKLOAD
     x, ref = WL.sg_inputs(w["channels"], w["map_h"], w["map_w"], seed=w["seed"])
