@@ -318,8 +318,8 @@ def main() -> int:
     # structure-guidance blend: reads x and ref, writes out, 4 bytes each per element
     sg_bytes = 12 * sgw["channels"] * sgw["map_h"] * sgw["map_w"]
 
-    # The blend is an ~8 us kernel: an event pair around each launch adds ~2 us to
-    # it, and a Python loop of launches cannot issue them that fast.  So it is
+    # The blend is a few-microsecond kernel: an event pair around each launch adds
+    # microseconds to it, and a Python loop of launches cannot issue them that fast.  So it is
     # also timed as 100 launches captured in one HIP graph, replayed between two
     # events.  An elementwise op that moves the same bytes (x + ref: reads both,
     # writes one array), timed the same way, gives the streaming floor of a
