@@ -358,6 +358,19 @@ def test_asg_blend(count):
     assert np.abs(out.cpu().numpy() - exp).max() <= 1e-6
 
 
+@pytest.mark.parametrize("target", ["eps", "eps_ref_prev", "mask"])
+def test_asg_blend_in_place(target):
+    """out may be any one of the inputs (the sampler updates eps in place): the
+    result equals the out-of-place call's, bit for bit."""
+    eps, ref, mask = WL.asg_inputs(((1 << 20) + 3,), seed=21)
+    dev = {n: torch.from_numpy(a).cuda() for n, a in (("eps", eps), ("eps_ref_prev", ref), ("mask", mask))}
+    want = npa.asg_blend(dev["eps"], dev["eps_ref_prev"], dev["mask"], 0.7)
+    got = npa.asg_blend(dev["eps"], dev["eps_ref_prev"], dev["mask"], 0.7, out=dev[target])
+    torch.cuda.synchronize()
+    assert got.data_ptr() == dev[target].data_ptr()
+    assert torch.equal(got, want)
+
+
 @pytest.mark.parametrize("spec,H,W,d", [(A.Windows(8, 8, 4, 4), 16, 16, 64), (A.Strips(2, halo_rows=3), 16, 16, 64),
                                         (A.Windows(8, 8, 4, 4), 16, 16, 128)])
 def test_late_large_logits_take_the_robust_pass(spec, H, W, d):
