@@ -110,7 +110,7 @@ constexpr int kMaxR = 16;
 constexpr float kTapScale = 1024.0f;
 constexpr int kPoolBytes = (kRows * kRows + kRows * kT) * 4;  // the fp32 form's diff + rows
 static_assert(kPoolBytes >= 2 * kRows * kPitch * 2, "hi/lo rows fit the pool");
-static_assert(2 * kMaxR <= kSgMaxRadius * 2, "taps in range");
+static_assert(kMaxR <= kSgMaxRadius, "every tap index the kernel reads lies in SgArgs::taps");
 
 // 8-element chunk q of staged row r sits at chunk q ^ swz(r): the 16 rows
 // 8u + 4h + i (u, i < 4) of one A operand get 16 distinct masks, so its 16
