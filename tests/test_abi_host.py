@@ -271,3 +271,33 @@ def test_window_mode_needs_no_stale(lib):
     hj = npa.make_halo(tile=(8, 8), halo=(4, 4), text_tokens=16)
     tiles, _ = npa.plan(Lj, hj)
     assert all(s["src"] == 0 for t in tiles for s in t["keys"])
+
+
+def test_last_error_is_per_thread(lib):
+    """npa_last_error() keeps one message per host thread: two threads failing
+    in different ways at the same time each read back their own message."""
+    import threading
+
+    L = npa.make_layout(1, 2, 64, 32, 32)
+    kinds = {
+        "shape": (npa.make_halo(strips=5, p=0.3), {}, npa.NPA_ERR_SHAPE, b"divide"),
+        "alias": (npa.make_halo(strips=4, p=0.3), {"out": (1 << 20) + 4096}, npa.NPA_ERR_INVALID_ARG, b"alias"),
+    }
+    start = threading.Barrier(2)
+    bad = []
+
+    def run(kind):
+        halo, kw, status, word = kinds[kind]
+        start.wait()
+        for _ in range(2000):
+            if _status(lib, L, halo, **kw) != status or word not in lib.npa_last_error():
+                bad.append(kind)
+                return
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in kinds]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad
+

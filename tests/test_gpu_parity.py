@@ -154,6 +154,43 @@ def test_repeated_calls_are_bitwise_identical(name):
                            first.view(torch.int16 if dt == torch.bfloat16 else torch.int32)), f"{name}: repeat {rep}"
 
 
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no device state between calls: a strip layer, a
+    d = 128 window layer and the blend issued on two streams at once (default
+    priority) give the same bits as each call made alone."""
+    print("[parity] two streams", flush=True)
+    names = ["sdxl2048_strips", "flux2048_strips"]
+    ts, kws, alone = [], [], []
+    for name in names:
+        w = WL.ATTENTION_WORKLOADS[name]
+        t = {n: (None if a is None else _dev(a, w["dtype"])) for n, a in WL.workload_inputs(name).items()}
+        kw = dict(WL.halo_kwargs(w), map_hw=(w["map_h"], w["map_w"]))
+        ts.append(t)
+        kws.append(kw)
+        alone.append(npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], **kw))
+    x, r = (torch.from_numpy(a).cuda() for a in WL.sg_inputs(4, 512, 512, seed=3))
+    sg_alone = npa.sg_blend(x, r, 0.5, 4.0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                t = ts[i]
+                outs.append((i, npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], **kws[i])))
+                if i == rep % 2:
+                    outs.append((2, npa.sg_blend(x, r, 0.5, 4.0)))
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for i, got in outs:
+        want = sg_alone if i == 2 else alone[i]
+        view = torch.int32 if want.dtype == torch.float32 else torch.int16
+        assert torch.equal(got.view(view), want.view(view)), f"call {i} differs on a shared GPU"
+
+
 # ----------------------------------------------------------- structural
 @pytest.mark.parametrize("spec", [A.Strips(2, halo_rows=1), A.Strips(4, halo_rows=2), A.Strips(4, halo_rows=0),
                                   A.Windows(2, 2, 1, 1), A.Windows(1, 4, 2, 0)])
