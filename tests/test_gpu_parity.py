@@ -321,7 +321,10 @@ def test_sg_blend(shape, sigma, w):
      ((1, 1, 100, 128), 1.5, 0.7),    # R = 5: staged radius 8, taps shifted by 3
      ((1, 3, 130, 132), 5.25, 0.5),   # R = 16, the largest matrix-core radius
      ((2, 1, 64, 64), 0.3, 1.0),      # R = 1
-     ((1, 1, 17, 20), 4.0, -0.4)],    # a 17 x 20 image inside one tile
+     ((1, 1, 17, 20), 4.0, -0.4),     # a 17 x 20 image inside one tile
+     ((1, 2, 13, 16), 4.0, 0.5),      # H = R + 1, W = R + 4: the tightest one-reflection borders
+     ((1, 1, 72, 96), 2.5, 0.3),      # R = 8: no tap shift
+     ((2, 2, 40, 44), 0.5, 0.9)],     # R = 2: taps shifted by 2
 )
 def test_sg_blend_matrix_core_shapes(shape, sigma, w):
     """Shapes the matrix-core blend takes (W a multiple of 4, R <= 16): tile
