@@ -302,6 +302,92 @@ def test_nan_poisoning_at_full_size(name):
         del q, k, v, ks, vs, got
 
 
+# ------------------------------------- robust pass and NaN keys, full size
+ROBUST = ["sdxl4096_npa", "flux4096_npa", "flux4096_joint", "sdxl2048_strips"]
+
+
+def _planted(w, spec):
+    """Stored-token indices of two map keys: the map's centre and a token one
+    row above and one column left of the bottom-right corner."""
+    T = A.text_tokens(spec)
+    H, W = w["map_h"], w["map_w"]
+    return [T + (H // 2) * W + W // 2, T + (H - 2) * W + (W - 2)]
+
+
+def _tiles_holding(spec, H, W, key):
+    """Query tokens of every tile whose fresh key set holds `key`."""
+    return [qt for qt, ft, _ in A.iter_tiles(H, W, spec) if key in set(ft.tolist())]
+
+
+@pytest.mark.parametrize("name", ROBUST)
+def test_robust_pass_at_full_size(name):
+    """Two keys per (batch, head) whose logits beat the rest by 180-280 log2
+    units (q and k share a large first channel): past 2^128 the fixed-shift
+    weights overflow fp32, so every workgroup whose key set holds one of them,
+    after its first 32 keys, gives inf/inf unless it redoes its tile with the
+    true row maxima -- a pass that walks the same copy cursor over the full
+    layer's key runs.  The affected tiles and one unaffected tile, for two
+    (batch, head) pairs, against the oracle."""
+    w = WL.ATTENTION_WORKLOADS[name]
+    print(f"[probe] robust pass {name}", flush=True)
+    spec = _spec(w)
+    H, W = w["map_h"], w["map_w"]
+    inp = WL.workload_inputs(name)
+    q, k = inp["q"].copy(), inp["k"].copy()
+    q[:, :, :, 0] = 40.0
+    keys = _planted(w, spec)
+    for key in keys:
+        k[:, key, :, 0] = 40.0
+    t = {n: (None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(TDT[w["dtype"]]))
+         for n, a in dict(inp, q=q, k=k).items()}
+    out = npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], map_hw=(H, W), **_kw(spec))
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    sel = set()
+    for key in keys:
+        for qt in _tiles_holding(spec, H, W, key):
+            sel |= set(qt.tolist())
+    sel |= set(next(iter(A.iter_tiles(H, W, spec)))[0].tolist())  # the first map tile: no planted key
+    qs = np.array(sorted(sel))
+    heads = [(0, 0), (w["batch"] - 1, w["heads"] - 1)]
+    ref = A.attention_tier1(q, k, inp["v"], inp["k_stale"], inp["v_stale"], H, W, spec, query_tokens=qs, heads=heads)
+    for b, j in heads:
+        err = np.abs(got[b, qs, j] - ref[b, qs, j]).max()
+        assert err <= ATOL[w["dtype"]], f"{name} (b={b}, head={j}): max abs err {err}"
+    del t, out
+
+
+@pytest.mark.parametrize("name", ["sdxl4096_npa", "flux4096_joint", "sdxl2048_strips"])
+def test_nan_key_reaches_exactly_its_sets(name):
+    """One NaN in a fresh key row of one (batch, head): the outputs that turn
+    NaN are exactly those of the queries whose key set holds that key, in that
+    (batch, head); every other output is finite and bit-identical to the clean
+    run."""
+    w = WL.ATTENTION_WORKLOADS[name]
+    print(f"[probe] NaN key {name}", flush=True)
+    spec = _spec(w)
+    H, W = w["map_h"], w["map_w"]
+    inp = WL.workload_inputs(name)
+    dt = TDT[w["dtype"]]
+    t = {n: (None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dt)) for n, a in inp.items()}
+    kw = dict(_kw(spec), map_hw=(H, W))
+    clean = npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], **kw)
+    key = _planted(w, spec)[0]
+    b, j = w["batch"] - 1, w["heads"] // 2
+    t["k"][b, key, j, 5] = float("nan")
+    got = npa.attn_fwd(t["q"], t["k"], t["v"], t["k_stale"], t["v_stale"], **kw)
+    torch.cuda.synchronize()
+    expect = torch.zeros(got.shape[:3], dtype=torch.bool)
+    for qt in _tiles_holding(spec, H, W, key):
+        expect[b, torch.from_numpy(qt), j] = True
+    nan = torch.isnan(got.float()).any(dim=-1).cpu()
+    assert torch.equal(nan, expect), f"{name}: {int(nan.sum())} NaN rows, {int(expect.sum())} expected"
+    assert bool(torch.isnan(got.float()[expect.to(got.device)]).all())
+    keep = ~expect.to(got.device)
+    assert torch.equal(got[keep].view(torch.int16), clean[keep].view(torch.int16))
+    del t, clean, got
+
+
 # --------------------------------------------- window rows of 32..96 keys
 # (H, W, spec): the widest window row of each case is 32, 33, 48, 63, 64 or 96
 # keys; the border tiles' rows are narrower (24 .. 80), some windows end on a
