@@ -198,9 +198,20 @@ __device__ __forceinline__ void exp_pack0(const f32x4& a0, const f32x4& a1, bf16
 // single-run cursor).
 constexpr int kModeJoint = 2;
 
+// Every 32-bit word of the kernel arguments into scalar registers at once: one
+// batch of scalar loads at the start instead of a chain of dependent ones
+// spread over the prologue's branches.
+template <typename T>
+__device__ __forceinline__ void load_args_now(const T& a) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&a);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
+}
+
 template <int D, int MODE, bool PARTIAL, bool SMALL>
 __global__ __launch_bounds__((64 * Cfg<D, SMALL>::WAVES), (Cfg<D, SMALL>::MINB)) void attn_bf16_kernel(
     const AttnArgs a) {
+  load_args_now(a);
   constexpr bool kWin = MODE != NPA_MODE_STRIPS;  // map tiles are 2-D windows
   constexpr bool kRuns = MODE != NPA_MODE_WINDOW;  // more than one key run per tile
   constexpr int kWaves = Cfg<D, SMALL>::WAVES;
