@@ -103,6 +103,7 @@ npa_status_t make_geo(const npa_layout_t* L, const npa_halo_t* h, npa::Geo* g) {
     g->eh = h->halo_h < L->map_h ? h->halo_h : L->map_h;
     g->ew = h->halo_w < L->map_w ? h->halo_w : L->map_w;
     g->tiles_x = L->map_w / h->tile_w;
+    g->by_tiles_x = npa::DivBy::of(g->tiles_x);
     g->T = h->text_tokens;
     g->n_img = (L->map_h / h->tile_h) * g->tiles_x;
     g->n_tiles = g->n_img + (g->T > 0 ? 1 : 0);
@@ -318,6 +319,7 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
     return fail(NPA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)nblocks);
   a.nblocks = (int32_t)nblocks;
   a.text_blocks = (int32_t)text_blocks;
+  npa::set_divisors(a);
   float scale = L->scale;
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L->head_dim));
   if (!std::isfinite(scale)) return fail(NPA_ERR_INVALID_ARG, "scale must be finite");

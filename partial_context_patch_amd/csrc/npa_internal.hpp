@@ -10,6 +10,29 @@
 
 namespace npa {
 
+// Division by a divisor that is fixed for a whole launch, as a multiply-high,
+// an add and a shift (division by invariant integers, Granlund and Montgomery,
+// PLDI 1994): for 1 <= d < 2^31 let s = ceil(log2 d) and m = ceil(2^(32+s) / d),
+// which lies in [2^32, 2^33); then n / d = floor(n * m / 2^(32+s)) for every
+// 0 <= n < 2^31, because m * d - 2^(32+s) < d <= 2^s.  m - 2^32 is stored, so
+// floor(n * m / 2^32) = mulhi(n, m - 2^32) + n, which stays below 2^32.  In the
+// kernels the divisors are uniform: three scalar instructions instead of the
+// ~30 of a general 32-bit division (with a round trip through the vector unit).
+struct DivBy {
+  uint32_t d, m, s;
+  static DivBy of(int32_t divisor) {  // host: 1 <= divisor < 2^31
+    DivBy r{(uint32_t)divisor, 0, 0};
+    while ((1u << r.s) < r.d) ++r.s;
+    r.m = (uint32_t)((((uint64_t)1 << (32 + r.s)) + r.d - 1) / r.d - ((uint64_t)1 << 32));
+    return r;
+  }
+  NPA_HD int32_t div(int32_t n) const {  // 0 <= n < 2^31
+    const uint32_t u = (uint32_t)n;
+    return (int32_t)(((uint32_t)(((uint64_t)u * m) >> 32) + u) >> s);
+  }
+  NPA_HD int32_t mod(int32_t n) const { return n - div(n) * (int32_t)d; }
+};
+
 // Validated plan parameters.  Tiles are enumerated in closed form from these,
 // on the host by the planner and on the device by each workgroup, so no tile
 // table ever lives in device memory.
@@ -23,6 +46,7 @@ struct Geo {
   int32_t T;         // window: text tokens stored before the map's tokens
   int32_t n_img;     // map tiles; the text tile (T > 0) is tile n_img
   int32_t n_tiles;   // n_img, plus one when T > 0
+  DivBy by_tiles_x;  // window: division by tiles_x (set by set_divisors)
 };
 
 // A run of tokens: `rows` runs of `row_len` tokens, first at `start`, `pitch` apart.
@@ -70,7 +94,7 @@ NPA_HD TileRuns tile_runs(const Geo& g, int32_t tile) {
     t.k[2] = Run{0, 0, 0, 0};
     t.src[2] = 0;
   } else {
-    const int32_t ti = tile / g.tiles_x, tj = tile - ti * g.tiles_x;
+    const int32_t ti = g.by_tiles_x.div(tile), tj = tile - ti * g.tiles_x;
     const int32_t r0 = imax(0, ti * g.th - g.eh), r1 = imin(g.H, (ti + 1) * g.th + g.eh);
     const int32_t c0 = imax(0, tj * g.tw - g.ew), c1 = imin(g.W, (tj + 1) * g.tw + g.ew);
     t.q = Run{g.T + ti * g.th * g.W + tj * g.tw, g.tw, g.th, g.W};
@@ -109,7 +133,20 @@ struct AttnArgs {
   float c;          // scale * log2(e)
   uint32_t range_bytes;  // bytes spanned by one (batch, head) slice: ((N-1)*sn + d) * esize
   int32_t partial;       // some key run is not a multiple of 64 keys
+  // division by qblocks, text_qblocks (1 when 0), n_img, Hh and B * Hh (set by set_divisors)
+  DivBy by_qblocks, by_text_qblocks, by_n_img, by_hh, by_bh;
 };
+
+// The division constants of a and a.g, from their plain fields (host side).
+inline void set_divisors(AttnArgs& a) {
+  auto pos = [](int32_t v) { return v > 0 ? v : 1; };
+  a.g.by_tiles_x = DivBy::of(pos(a.g.tiles_x));
+  a.by_qblocks = DivBy::of(pos(a.qblocks));
+  a.by_text_qblocks = DivBy::of(pos(a.text_qblocks));
+  a.by_n_img = DivBy::of(pos(a.g.n_img));
+  a.by_hh = DivBy::of(pos(a.Hh));
+  a.by_bh = DivBy::of(pos(a.B * a.Hh));
+}
 
 // Which (query block, tile, head, batch) workgroup i of the grid computes.
 // The text tile's workgroups come first: each one walks every stored token,
@@ -146,35 +183,38 @@ NPA_HD BlockCoord decode_block(const AttnArgs& a, int32_t i, bool remap) {
   int32_t rest;
   const int32_t j = i - a.text_blocks;
   if (i < a.text_blocks) {
-    c.qb = i % a.text_qblocks;
-    rest = i / a.text_qblocks;
+    rest = a.by_text_qblocks.div(i);
+    c.qb = i - rest * a.text_qblocks;
     c.tile = a.g.n_img;
   } else if (!remap || a.g.mode != NPA_MODE_STRIPS) {
     const int32_t jj = remap ? xcd_remap(j, a.nblocks - a.text_blocks) : j;
-    c.qb = jj % a.qblocks;
-    rest = jj / a.qblocks;
-    c.tile = rest % a.g.n_img;
-    rest /= a.g.n_img;
+    rest = a.by_qblocks.div(jj);
+    c.qb = jj - rest * a.qblocks;
+    const int32_t r2 = a.by_n_img.div(rest);
+    c.tile = rest - r2 * a.g.n_img;
+    rest = r2;
   } else {
     // units (rank, batch * heads + head), rank slowest; the first 8*floor(U/8)
     // units are dealt round-robin over the XCDs, the rest (the smallest) in order
-    const int32_t units = (a.nblocks - a.text_blocks) / a.qblocks;
+    const int32_t units = a.by_qblocks.div(a.nblocks - a.text_blocks);
     const int32_t dealt = (units & ~7) * a.qblocks;
     int32_t unit;
     if (j < dealt) {
       const int32_t k = j >> 3;
-      unit = (k / a.qblocks) * 8 + (j & 7);
-      c.qb = k % a.qblocks;
+      const int32_t kq = a.by_qblocks.div(k);
+      unit = kq * 8 + (j & 7);
+      c.qb = k - kq * a.qblocks;
     } else {
-      unit = (units & ~7) + (j - dealt) / a.qblocks;
-      c.qb = (j - dealt) % a.qblocks;
+      const int32_t jq = a.by_qblocks.div(j - dealt);
+      unit = (units & ~7) + jq;
+      c.qb = (j - dealt) - jq * a.qblocks;
     }
-    const int32_t bh = a.B * a.Hh;
-    c.tile = border_last(unit / bh, a.g.n_img);
-    rest = unit % bh;
+    const int32_t rank = a.by_bh.div(unit);
+    c.tile = border_last(rank, a.g.n_img);
+    rest = unit - rank * (a.B * a.Hh);
   }
-  c.head = rest % a.Hh;
-  c.b = rest / a.Hh;
+  c.b = a.by_hh.div(rest);
+  c.head = rest - c.b * a.Hh;
   return c;
 }
 

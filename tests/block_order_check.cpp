@@ -20,6 +20,7 @@ static bool check(int mode, int B, int Hh, int nr, int nc, int qblocks, int text
   a.text_qblocks = text_qblocks;
   a.text_blocks = B * Hh * text_qblocks;
   a.nblocks = a.text_blocks + B * Hh * a.g.n_img * qblocks;
+  set_divisors(a);
   const int tiles = a.g.n_img + (text_qblocks > 0);
   std::vector<int> seen((size_t)B * Hh * tiles * (qblocks > text_qblocks ? qblocks : text_qblocks), 0);
   for (int i = 0; i < a.nblocks; ++i) {
