@@ -467,7 +467,7 @@ def test_f32_wide_window_rows(H, W, spec, shape):
 
 
 # ------------------------------------------------- fp32 at layer sizes
-@pytest.mark.parametrize("name", ["sdxl4096_npa", "sdxl2048_strips", "sdxl1024_strips"])
+@pytest.mark.parametrize("name", ["sdxl4096_npa", "flux4096_npa", "sdxl2048_strips", "sdxl1024_strips"])
 def test_f32_at_layer_size(name):
     """fp32 inputs of the bf16 layers' shapes (the sizes the fp32 throughput is
     quoted on): every query of the first and the last (batch, head) slice, and
