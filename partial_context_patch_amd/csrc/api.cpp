@@ -319,6 +319,13 @@ npa_status_t npa_attn_fwd(const void* Q, const void* K_fresh, const void* V_fres
     return fail(NPA_ERR_SHAPE, "grid of %lld workgroups is too large", (long long)nblocks);
   a.nblocks = (int32_t)nblocks;
   a.text_blocks = (int32_t)text_blocks;
+  // windows whose halo is small against the tile (window area <= 2.25x the
+  // tile's) share little between neighbouring tiles: list the longest tiles first
+  a.largest_first = 0;
+  if (g.mode == NPA_MODE_WINDOW && g.tiles_x >= 3 && g.n_img / g.tiles_x >= 3) {
+    const int64_t win = (int64_t)(g.th + 2 * g.eh) * (g.tw + 2 * g.ew), tile = (int64_t)g.th * g.tw;
+    a.largest_first = (4 * win <= 9 * tile) ? 1 : 0;
+  }
   npa::set_divisors(a);
   float scale = L->scale;
   if (!(scale > 0.0f)) scale = (float)(1.0 / std::sqrt((double)L->head_dim));

@@ -135,6 +135,8 @@ struct AttnArgs {
   int32_t partial;       // some key run is not a multiple of 64 keys
   // division by qblocks, text_qblocks (1 when 0), n_img, Hh and B * Hh (set by set_divisors)
   DivBy by_qblocks, by_text_qblocks, by_n_img, by_hh, by_bh;
+  int32_t largest_first;  // window tiles listed interior, edge, corner (see decode_block)
+  DivBy by_inner_x;       // division by tiles_x - 2
 };
 
 // The division constants of a and a.g, from their plain fields (host side).
@@ -146,6 +148,38 @@ inline void set_divisors(AttnArgs& a) {
   a.by_n_img = DivBy::of(pos(a.g.n_img));
   a.by_hh = DivBy::of(pos(a.Hh));
   a.by_bh = DivBy::of(pos(a.B * a.Hh));
+  a.by_inner_x = DivBy::of(pos(a.g.tiles_x - 2));
+}
+
+// Window tile of rank r when the tiles of a head are listed interior first, then
+// edge tiles, then the four corners (tiles_x, tiles_y >= 3): the windows clipped
+// by the border (fewer keys) come last.
+template <class A>
+NPA_HD int32_t tile_by_class(const A& a, int32_t r) {
+  const int32_t tx = a.g.tiles_x, ty = a.g.n_img / tx, ix = tx - 2, iy = ty - 2;
+  const int32_t n0 = ix * iy, n1 = 2 * ix + 2 * iy;
+  int32_t ti, tj;
+  if (r < n0) {
+    ti = a.by_inner_x.div(r);
+    tj = 1 + (r - ti * ix);
+    ti += 1;
+  } else if (r < n0 + n1) {
+    const int32_t e = r - n0;
+    if (e < ix) {
+      ti = 0, tj = 1 + e;
+    } else if (e < 2 * ix) {
+      ti = ty - 1, tj = 1 + (e - ix);
+    } else if (e < 2 * ix + iy) {
+      ti = 1 + (e - 2 * ix), tj = 0;
+    } else {
+      ti = 1 + (e - 2 * ix - iy), tj = tx - 1;
+    }
+  } else {
+    const int32_t k = r - n0 - n1;
+    ti = (k >> 1) ? ty - 1 : 0;
+    tj = (k & 1) ? tx - 1 : 0;
+  }
+  return ti * tx + tj;
 }
 
 // Which (query block, tile, head, batch) workgroup i of the grid computes.
@@ -157,7 +191,10 @@ inline void set_divisors(AttnArgs& a) {
 // `remap` the ids are regrouped so that all query blocks of a unit run on one
 // XCD (they share the unit's K/V through that XCD's L2):
 //   windows: each XCD runs one contiguous range of units, so neighbouring
-//            tiles of a head (whose windows overlap) share that L2 too;
+//            tiles of a head (whose windows overlap) share that L2 too; with
+//            `largest_first` (set by the host for windows at most 2.25x their
+//            tile's area, where neighbours share little) a head's tiles are
+//            listed interior, edge, corner, so each XCD ends on short units;
 //   strips:  units are listed interior strips first, border strips (one
 //            stale halo, fewer keys) last, and dealt round-robin over the
 //            XCDs; each XCD then runs its longest units first, which keeps the
@@ -192,6 +229,7 @@ NPA_HD BlockCoord decode_block(const AttnArgs& a, int32_t i, bool remap) {
     c.qb = jj - rest * a.qblocks;
     const int32_t r2 = a.by_n_img.div(rest);
     c.tile = rest - r2 * a.g.n_img;
+    if (remap && a.largest_first) c.tile = tile_by_class(a, c.tile);
     rest = r2;
   } else {
     // units (rank, batch * heads + head), rank slowest; the first 8*floor(U/8)
