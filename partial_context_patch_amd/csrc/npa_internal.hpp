@@ -164,15 +164,16 @@ NPA_HD int32_t tile_by_class(const A& a, int32_t r) {
     tj = 1 + (r - ti * ix);
     ti += 1;
   } else if (r < n0 + n1) {
+    // edge tiles in raster order: top row, then the left and right ends of
+    // each interior row, then the bottom row (neighbours stay together)
     const int32_t e = r - n0;
     if (e < ix) {
       ti = 0, tj = 1 + e;
-    } else if (e < 2 * ix) {
-      ti = ty - 1, tj = 1 + (e - ix);
-    } else if (e < 2 * ix + iy) {
-      ti = 1 + (e - 2 * ix), tj = 0;
+    } else if (e < ix + 2 * iy) {
+      const int32_t k = e - ix;
+      ti = 1 + (k >> 1), tj = (k & 1) ? tx - 1 : 0;
     } else {
-      ti = 1 + (e - 2 * ix - iy), tj = tx - 1;
+      ti = ty - 1, tj = 1 + (e - ix - 2 * iy);
     }
   } else {
     const int32_t k = r - n0 - n1;
